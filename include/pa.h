@@ -1,0 +1,212 @@
+/*
+ * pa.h -- paged-KV decode attention for MI355X (gfx950): the C ABI of libpa.so.
+ *
+ * What is computed (by page title and section):
+ *   "19.2 KV Cache 系统化管理" §19.2.2 and §19.2.3: the keys and values of all
+ *   requests live in two pools of fixed-size physical blocks, each shaped
+ *   [num_blocks, block_size, num_kv_heads, head_dim]; a request's block
+ *   table maps its logical block i (tokens i*block_size ...) to a physical
+ *   block; attention of a query walks the request's blocks in order and
+ *   folds them into a running maximum, running sum and running weighted sum
+ *   (online softmax), then divides -- which equals ordinary softmax
+ *   attention over the request's tokens.
+ *   "LLM 推理引擎的内存管理与调度" §3: the kernel finds a token through the
+ *   block table (logical block -> physical block) plus its in-block offset.
+ *   §4 of that page and §19.2.2 above: blocks are shared between requests
+ *   with reference counts and copied on the first diverging write.
+ *   §8 of that page: a long prompt is processed in chunks whose query tokens
+ *   attend to the cached context and, causally, to each other.
+ *
+ * Conventions shared by every call.
+ *   - Device pointers name caller-owned device memory (hipMalloc or a torch
+ *     tensor); arrays are dense and row-major with the shapes given below.
+ *     The library never allocates or frees device memory, never
+ *     synchronizes and never reads device memory on the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls are asynchronous and ordered on that stream.
+ *   - Every call returns a pa_status; on anything but PA_OK,
+ *     pa_last_error() returns a message for the calling thread and no
+ *     kernel was launched (PA_ERR_HIP: the launch itself failed).
+ *   - Host-side arguments (sizes, null pointers, supported shapes) are
+ *     validated.  Device-side contents are the caller's contract: block-table
+ *     entries of the logical blocks a sequence uses must lie in
+ *     [0, num_blocks) and seq_lens in [0, max_blocks_per_seq*block_size].
+ *     Violations give unspecified results, but the kernels clamp every index
+ *     they derive from device data, so no access leaves the arrays passed.
+ *   - Supported shapes: dtype PA_F32 or PA_BF16; head_dim 32, 64, 128 or
+ *     256; block_size a power of two from 1 to 256; num_q_heads /
+ *     num_kv_heads in {1, 2, 4, 8}.
+ *   - Softmax scores are scale * dot(q, k); every workload passes
+ *     1/sqrt(head_dim), the value the pages use.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,    /* null pointer, bad size, inconsistent shapes */
+  PA_ERR_UNSUPPORTED = 2,    /* valid but not built: dtype/head_dim/GQA ratio */
+  PA_ERR_NO_FREE_BLOCKS = 3, /* the pool's free list cannot cover the request */
+  PA_ERR_HIP = 4,            /* a HIP runtime call or kernel launch failed */
+  PA_ERR_NOT_FOUND = 5       /* unknown sequence handle */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Shape of the two KV pools (K and V share it): [num_blocks, block_size,
+ * num_kv_heads, head_dim] elements of `dtype`.  "19.2 KV Cache 系统化管理"
+ * §19.2.3 gives this layout for its PhysicalBlockPool. */
+typedef struct {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype; /* pa_dtype */
+} pa_kv_layout;
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* pa_last_error(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device calls                                                              */
+/* ------------------------------------------------------------------------ */
+
+/* Cache write ("19.2 KV Cache 系统化管理" §19.2.3, write_slot/append_token):
+ * for every token t with slot s = slot_mapping[t] >= 0,
+ *   k_pool[s / block_size, s % block_size, :, :] = k_new[t, :, :]   (and V).
+ *   k_new, v_new : [num_tokens, num_kv_heads, head_dim], pool dtype
+ *   slot_mapping : device int32 [num_tokens]; s = physical*block_size+offset;
+ *                  negative = skip (padding); s >= num_blocks*block_size is
+ *                  skipped as well.
+ * Two tokens with the same slot in one call: which one lands is unspecified.
+ * num_tokens == 0 is a no-op. */
+pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                      const void* k_new, const void* v_new,
+                      const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* Whole-block copies, the copy step of copy-on-write ("19.2 KV Cache
+ * 系统化管理" §19.2.2): for every pair i, pool[dst_i] = pool[src_i] for K and V.
+ *   pairs : device int32 [num_pairs, 2] as (src, dst).
+ * Destinations must be distinct and must not be sources in the same call
+ * (the block pool never produces such pairs); out-of-range ids are skipped. */
+pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* Single-pass paged decode ("19.2 KV Cache 系统化管理" §19.2.3,
+ * paged_attention): one query token per sequence, at position seq_len-1,
+ * attending to keys 0 .. seq_len-1 of its own table.
+ *   q, out       : [num_seqs, num_q_heads, head_dim], pool dtype; query head h
+ *                  reads KV head h / (num_q_heads/num_kv_heads)
+ *   block_tables : device int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens     : device int32 [num_seqs] (tokens in the cache, including
+ *                  this step's token); seq_len 0 gives a zero row
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even. */
+pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q,
+                    const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                    float scale, void* stream);
+
+/* Split-sequence paged attention, first pass.  The keys a query sees are cut
+ * into partitions of `partition_size` tokens (partition p = keys
+ * [p*P, min((p+1)*P, key_end))); each partition is summarised by
+ *   part_o[j, h, p, :] = softmax-weighted mean of its values   (fp32)
+ *   part_lse[j, h, p]  = log(sum over its keys of exp(scale*q.k)) (natural log)
+ * which pa_reduce merges.  This is the running max/sum recurrence of the
+ * pages' online softmax with one partition as the unit.
+ *   q            : [num_q_tokens, num_q_heads, head_dim], pool dtype
+ *   cu_q_lens    : device int32 [num_seqs+1] prefix sums of query tokens per
+ *                  sequence, or NULL when each sequence has exactly one
+ *                  (then num_q_tokens == num_seqs).  A sequence's query
+ *                  tokens are its last q_len tokens; query i sits at
+ *                  position seq_len - q_len + i and sees keys 0 .. position
+ *                  (chunked prefill, "LLM 推理引擎的内存管理与调度" §8).
+ *   part_o       : fp32 [num_q_tokens, num_q_heads, max_partitions, head_dim]
+ *   part_lse     : fp32 [num_q_tokens, num_q_heads, max_partitions]
+ * A query of a single-query sequence has ceil(key_end/partition_size)
+ * partitions; every query of a multi-query sequence has exactly one
+ * partition covering all the keys it sees.  Only those entries are written.
+ * Requires partition_size % block_size == 0, partition_size % 16 == 0 and
+ * max_partitions*partition_size >= max_blocks_per_seq*block_size. */
+pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,
+                          int32_t max_partitions, int32_t partition_size,
+                          const void* q, const int32_t* cu_q_lens, int32_t num_q_tokens,
+                          const void* k_pool, const void* v_pool,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                          float scale, void* stream);
+
+/* Split-sequence paged attention, second pass: log-sum-exp merge of the
+ * partitions pa_decode_split wrote (same partition rule).  With L = log sum_p
+ * exp(lse_p):  out[j, h, :] = sum_p exp(lse_p - L) * o_p,  lse_out[j, h] = L.
+ *   out     : [num_q_tokens, num_q_heads, head_dim] of out_dtype
+ *   lse_out : fp32 [num_q_tokens, num_q_heads] or NULL
+ * A query with no key gets a zero row and lse -inf. */
+pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out,
+                    const float* part_o, const float* part_lse,
+                    int32_t max_partitions, int32_t partition_size,
+                    const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                    void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block pool ("19.2 KV Cache 系统化管理" §19.2.2-§19.2.3)               */
+/* ------------------------------------------------------------------------ */
+/* A library-owned host object: a LIFO free list of physical block ids,
+ * one reference count per block, and per-sequence block tables.  Not
+ * thread-safe (one scheduler thread drives it).  Calls are all-or-nothing:
+ * on any error the pool is unchanged. */
+typedef struct pa_pool pa_pool;
+
+/* initial_free: host int32 [num_blocks], a permutation of 0..num_blocks-1
+ * popped from its END (NULL = ascending order, so block num_blocks-1 is
+ * handed out first, as in the pages' example). */
+pa_status pa_pool_create(int32_t num_blocks, int32_t block_size,
+                         const int32_t* initial_free, pa_pool** out);
+void pa_pool_destroy(pa_pool* pool);
+int32_t pa_pool_num_free(const pa_pool* pool);               /* -1 if pool is NULL */
+int32_t pa_pool_refcount(const pa_pool* pool, int32_t block); /* -1 if out of range */
+/* Copy the free list (bottom to top) into host `out` (capacity `cap`). */
+pa_status pa_pool_free_list(const pa_pool* pool, int32_t* out, int32_t cap, int32_t* n);
+
+/* New empty sequence; its handle is written to *seq. */
+pa_status pa_seq_new(pa_pool* pool, int32_t* seq);
+/* New sequence sharing every block of `parent` (reference count + 1 each). */
+pa_status pa_seq_fork(pa_pool* pool, int32_t parent, int32_t* child);
+/* Blocks pa_seq_append(seq, n_tokens) would take from the free list. */
+pa_status pa_seq_blocks_needed(const pa_pool* pool, int32_t seq, int32_t n_tokens,
+                               int32_t* needed);
+/* Reserve slots for n_tokens new tokens of `seq`.  Writes one flat slot
+ * (physical*block_size + offset) per token to host slot_mapping_out
+ * [n_tokens].  When the first token lands in a partly filled block shared
+ * with another sequence, that block is copied first: a new block is taken,
+ * the table remapped, the old count lowered, and the pair (old, new) written
+ * to host cow_pairs_out [cow_cap, 2]; *n_cow gets the count (0 or 1).  The
+ * caller copies those blocks (pa_copy_blocks) before writing the tokens.
+ * PA_ERR_NO_FREE_BLOCKS if the free list is short (nothing changes). */
+pa_status pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens,
+                        int32_t* slot_mapping_out, int32_t* cow_pairs_out,
+                        int32_t cow_cap, int32_t* n_cow);
+/* Release every block of `seq` in logical order (counts - 1; a block whose
+ * count reaches 0 is appended to the free list) and forget the sequence. */
+pa_status pa_seq_release(pa_pool* pool, int32_t seq);
+pa_status pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len);
+/* Host int32 out[n, max_blocks]: row i = table of seqs[i], padded with fill. */
+pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
+                          int32_t max_blocks, int32_t fill, int32_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

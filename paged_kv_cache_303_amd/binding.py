@@ -1,0 +1,342 @@
+"""ctypes binding of libpa.so: the C ABI with the same names, torch for memory.
+
+Argument marshalling only -- every step of the attention path runs in the HIP
+kernels of ``libpa.so``; there is no CPU fallback.  Device arrays are torch
+tensors on the current HIP device (contiguous, of the dtypes the ABI names),
+and device calls are enqueued on ``torch.cuda.current_stream()``.  A non-OK
+status raises :class:`PagedAttentionError` (``NoFreeBlocks`` for an exhausted
+pool) with the library's message, as the pages' allocator raises a
+``RuntimeError`` when no block is left ("19.2 KV Cache 系统化管理" §19.2.3).
+
+The library must be loaded after ``torch`` so that it binds to the HIP
+runtime torch already loaded (same soname), and therefore to torch's streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import build as _build
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCKS, PA_ERR_HIP, \
+    PA_ERR_NOT_FOUND = range(6)
+PA_F32, PA_BF16 = 0, 1
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class NoFreeBlocks(PagedAttentionError):
+    pass
+
+
+class KVLayout(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_i32 = ctypes.c_int32
+_p = ctypes.c_void_p
+_pi32 = ctypes.POINTER(ctypes.c_int32)
+_f32 = ctypes.c_float
+_LAYOUT = ctypes.POINTER(KVLayout)
+
+_SIGNATURES = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_version": (ctypes.c_char_p, []),
+    "pa_kv_write": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p]),
+    "pa_copy_blocks": (_i32, [_LAYOUT, _p, _p, _p, _i32, _p]),
+    "pa_decode": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p]),
+    "pa_decode_split": (_i32, [_LAYOUT, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p,
+                               _i32, _i32, _f32, _p]),
+    "pa_reduce": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]),
+    "pa_pool_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
+    "pa_pool_destroy": (None, [_p]),
+    "pa_pool_num_free": (_i32, [_p]),
+    "pa_pool_refcount": (_i32, [_p, _i32]),
+    "pa_pool_free_list": (_i32, [_p, _pi32, _i32, _pi32]),
+    "pa_seq_new": (_i32, [_p, _pi32]),
+    "pa_seq_fork": (_i32, [_p, _i32, _pi32]),
+    "pa_seq_blocks_needed": (_i32, [_p, _i32, _i32, _pi32]),
+    "pa_seq_append": (_i32, [_p, _i32, _i32, _pi32, _pi32, _i32, _pi32]),
+    "pa_seq_release": (_i32, [_p, _i32]),
+    "pa_seq_len": (_i32, [_p, _i32, _pi32]),
+    "pa_block_tables": (_i32, [_p, _pi32, _i32, _i32, _i32, _pi32]),
+}
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        path = _build.library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               "`python -m paged_kv_cache_303_amd.build`")
+        handle = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def version() -> str:
+    return lib().pa_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != PA_OK:
+        msg = lib().pa_last_error().decode(errors="replace")
+        cls = NoFreeBlocks if status == PA_ERR_NO_FREE_BLOCKS else PagedAttentionError
+        raise cls(status, msg)
+
+
+# --- device calls -------------------------------------------------------------
+
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name, dtype=None):
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtype)
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def layout_of(k_pool: torch.Tensor) -> KVLayout:
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_blocks, block_size, num_kv_heads, head_dim]")
+    if k_pool.dtype not in _DTYPES:
+        raise TypeError(f"unsupported pool dtype {k_pool.dtype}")
+    nb, bs, hkv, d = k_pool.shape
+    return KVLayout(nb, bs, hkv, d, _DTYPES[k_pool.dtype])
+
+
+def _pools(k_pool, v_pool):
+    if v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must have the same shape and dtype")
+    return layout_of(k_pool), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool")
+
+
+def kv_write(k_pool, v_pool, k_new, v_new, slot_mapping) -> None:
+    """``pa_kv_write``: pool[slot // bs, slot % bs] = new[t] for slot >= 0."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    n = int(slot_mapping.shape[0])
+    row = (lay.num_kv_heads, lay.head_dim)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (n, *row):
+            raise ValueError(f"{name} must be [num_tokens, num_kv_heads, head_dim]")
+    _check(lib().pa_kv_write(ctypes.byref(lay), kp, vp, _dev(k_new, "k_new", k_pool.dtype),
+                             _dev(v_new, "v_new", k_pool.dtype),
+                             _dev(slot_mapping, "slot_mapping", torch.int32), n, _stream()))
+
+
+def copy_blocks(k_pool, v_pool, pairs) -> None:
+    """``pa_copy_blocks``: pool[dst] = pool[src] for every (src, dst) row of ``pairs``."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    _check(lib().pa_copy_blocks(ctypes.byref(lay), kp, vp, _dev(pairs, "pairs", torch.int32),
+                                int(pairs.shape[0]), _stream()))
+
+
+def _tables(block_tables, seq_lens, num_seqs):
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if tuple(seq_lens.shape) != (num_seqs,):
+        raise ValueError("seq_lens must be [num_seqs]")
+    return (_dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+            _dev(seq_lens, "seq_lens", torch.int32))
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None):
+    """``pa_decode``: one query per sequence, single pass.  Returns ``out``."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != lay.head_dim:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    bt, mb, sl = _tables(block_tables, seq_lens, b)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    _check(lib().pa_decode(ctypes.byref(lay), _dev(out, "out", k_pool.dtype),
+                           _dev(q, "q", k_pool.dtype), kp, vp, bt, mb, sl, b, hq, float(scale),
+                           _stream()))
+    return out
+
+
+def max_partitions_for(max_blocks: int, block_size: int, partition_size: int) -> int:
+    return max(1, -(-(max_blocks * block_size) // partition_size))
+
+
+def decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                 partition_size: int = 512, cu_q_lens=None, part_o=None, part_lse=None,
+                 max_partitions=None):
+    """``pa_decode_split``: per-partition summaries.  Returns ``(part_o, part_lse)``."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != lay.head_dim:
+        raise ValueError("q must be [num_q_tokens, num_q_heads, head_dim]")
+    nq, hq = int(q.shape[0]), int(q.shape[1])
+    b = int(seq_lens.shape[0])
+    bt, mb, sl = _tables(block_tables, seq_lens, b)
+    if cu_q_lens is not None and tuple(cu_q_lens.shape) != (b + 1,):
+        raise ValueError("cu_q_lens must be [num_seqs + 1]")
+    if max_partitions is None:
+        max_partitions = max_partitions_for(mb, lay.block_size, partition_size)
+    shape_o = (nq, hq, max_partitions, lay.head_dim)
+    if part_o is None:
+        part_o = torch.empty(shape_o, dtype=torch.float32, device=q.device)
+    if part_lse is None:
+        part_lse = torch.empty(shape_o[:3], dtype=torch.float32, device=q.device)
+    if tuple(part_o.shape) != shape_o or tuple(part_lse.shape) != shape_o[:3]:
+        raise ValueError("partial buffers have the wrong shape")
+    _check(lib().pa_decode_split(ctypes.byref(lay), _dev(part_o, "part_o", torch.float32),
+                                 _dev(part_lse, "part_lse", torch.float32), int(max_partitions),
+                                 int(partition_size), _dev(q, "q", k_pool.dtype),
+                                 _opt(cu_q_lens, "cu_q_lens", torch.int32), nq, kp, vp, bt, mb, sl,
+                                 b, hq, float(scale), _stream()))
+    return part_o, part_lse
+
+
+def reduce(part_o, part_lse, seq_lens, partition_size: int, out_dtype=torch.bfloat16,
+           cu_q_lens=None, out=None, lse_out=None):
+    """``pa_reduce``: log-sum-exp merge of the partitions.  Returns ``out``."""
+    nq, hq, maxp, d = (int(x) for x in part_o.shape)
+    b = int(seq_lens.shape[0])
+    if out is None:
+        out = torch.empty((nq, hq, d), dtype=out_dtype, device=part_o.device)
+    if out.dtype not in _DTYPES or tuple(out.shape) != (nq, hq, d):
+        raise ValueError("out must be [num_q_tokens, num_q_heads, head_dim] f32/bf16")
+    _check(lib().pa_reduce(_dev(out, "out"), _DTYPES[out.dtype],
+                           _opt(lse_out, "lse_out", torch.float32),
+                           _dev(part_o, "part_o", torch.float32),
+                           _dev(part_lse, "part_lse", torch.float32), maxp, int(partition_size),
+                           _opt(cu_q_lens, "cu_q_lens", torch.int32),
+                           _dev(seq_lens, "seq_lens", torch.int32), b, nq, hq, d, _stream()))
+    return out
+
+
+def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                    partition_size: int = 512, cu_q_lens=None):
+    """Split pass + reduce: attention output of every query token."""
+    part_o, part_lse = decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale,
+                                    partition_size=partition_size, cu_q_lens=cu_q_lens)
+    return reduce(part_o, part_lse, seq_lens, partition_size, out_dtype=q.dtype,
+                  cu_q_lens=cu_q_lens)
+
+
+# --- host block pool ------------------------------------------------------------
+
+def _i32_array(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(_pi32)
+
+
+class BlockPool:
+    """The library's host block pool (free list, reference counts, tables)."""
+
+    def __init__(self, num_blocks: int, block_size: int, initial_free=None):
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+        handle = ctypes.c_void_p()
+        free = None if initial_free is None else _i32_array(initial_free)
+        if free is not None and free.shape != (self.num_blocks,):
+            raise ValueError("initial_free must hold num_blocks ids")
+        _check(lib().pa_pool_create(self.num_blocks, self.block_size,
+                                    None if free is None else _ptr32(free),
+                                    ctypes.byref(handle)))
+        self._h = handle
+
+    def close(self):
+        if self._h:
+            lib().pa_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(lib().pa_pool_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pa_pool_refcount(self._h, int(block)))
+
+    def free_list(self) -> list:
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().pa_pool_free_list(self._h, _ptr32(out), self.num_blocks, ctypes.byref(n)))
+        return out[: n.value].tolist()
+
+    def new_seq(self) -> int:
+        s = ctypes.c_int32()
+        _check(lib().pa_seq_new(self._h, ctypes.byref(s)))
+        return s.value
+
+    def fork(self, parent: int) -> int:
+        s = ctypes.c_int32()
+        _check(lib().pa_seq_fork(self._h, int(parent), ctypes.byref(s)))
+        return s.value
+
+    def blocks_needed(self, seq: int, n_tokens: int) -> int:
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_blocks_needed(self._h, int(seq), int(n_tokens), ctypes.byref(n)))
+        return n.value
+
+    def append(self, seq: int, n_tokens: int):
+        """Returns ``(slots int32[n_tokens], [(old, new)] copy-on-write pairs)``."""
+        slots = np.empty(max(int(n_tokens), 1), dtype=np.int32)
+        cow = np.empty(2, dtype=np.int32)
+        ncow = ctypes.c_int32()
+        _check(lib().pa_seq_append(self._h, int(seq), int(n_tokens), _ptr32(slots), _ptr32(cow),
+                                   1, ctypes.byref(ncow)))
+        pairs = [(int(cow[0]), int(cow[1]))] if ncow.value else []
+        return slots[: int(n_tokens)], pairs
+
+    def release(self, seq: int) -> None:
+        _check(lib().pa_seq_release(self._h, int(seq)))
+
+    def seq_len(self, seq: int) -> int:
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_len(self._h, int(seq), ctypes.byref(n)))
+        return n.value
+
+    def block_tables(self, seqs, max_blocks: int, fill: int = -1) -> np.ndarray:
+        s = _i32_array(seqs)
+        out = np.empty((len(s), int(max_blocks)), dtype=np.int32)
+        _check(lib().pa_block_tables(self._h, _ptr32(s), len(s), int(max_blocks), int(fill),
+                                     _ptr32(out)))
+        return out

@@ -1,0 +1,257 @@
+// C ABI entry points of libpa.so for the device calls: argument validation,
+// launch parameters, error reporting.  Kernels live in pa_decode.hip and
+// pa_cache.hip; the host block pool in pa_pool.cpp.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pa.h"
+#include "pa_error.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+thread_local std::string g_last_error;
+}
+
+pa_status fail(pa_status status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+namespace {
+
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int32_t log2i(int32_t x) {
+  int32_t r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+// Checks the pool layout; `what` names the calling entry point.
+pa_status check_layout(const pa_kv_layout* l, const char* what) {
+  if (!l) return fail(PA_ERR_INVALID_ARG, "%s: layout is NULL", what);
+  if (l->num_blocks <= 0 || l->block_size <= 0 || l->num_kv_heads <= 0 || l->head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout sizes must be positive", what);
+  if (l->dtype != PA_F32 && l->dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not PA_F32 or PA_BF16", what, l->dtype);
+  if (!pow2(l->block_size) || l->block_size > 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d is not a power of two <= 256", what,
+                l->block_size);
+  if (l->head_dim != 32 && l->head_dim != 64 && l->head_dim != 128 && l->head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {32, 64, 128, 256}", what,
+                l->head_dim);
+  const int64_t rows = (int64_t)l->num_blocks * l->block_size;
+  if (rows > (int64_t)INT32_MAX + 1)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_blocks*block_size exceeds the int32 slot range", what);
+  const int64_t block_bytes =
+      (int64_t)l->block_size * l->num_kv_heads * l->head_dim * (l->dtype == PA_BF16 ? 2 : 4);
+  if (block_bytes > (int64_t)1 << 30)
+    return fail(PA_ERR_UNSUPPORTED, "%s: one block exceeds 1 GiB", what);
+  return PA_OK;
+}
+
+pa_status check_heads(const pa_kv_layout* l, int32_t num_q_heads, const char* what) {
+  if (num_q_heads <= 0 || num_q_heads % l->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_q_heads %d is not a positive multiple of num_kv_heads %d",
+                what, num_q_heads, l->num_kv_heads);
+  const int32_t g = num_q_heads / l->num_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: query heads per KV head %d not in {1, 2, 4, 8}", what, g);
+  return PA_OK;
+}
+
+// KV heads handled by one workgroup (one wave each): the largest divisor of
+// num_kv_heads that is at most 4.
+int32_t waves_per_group(int32_t num_kv_heads) {
+  for (int32_t w = 4; w > 1; --w)
+    if (num_kv_heads % w == 0) return w;
+  return 1;
+}
+
+pa_status launch_status(pa_status st, const char* what) {
+  if (st == PA_ERR_UNSUPPORTED) return fail(st, "%s: no kernel instance for this shape", what);
+  if (st == PA_ERR_HIP) return fail(st, "%s: kernel launch failed", what);
+  return st;
+}
+
+}  // namespace
+}  // namespace pa
+
+using pa::fail;
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
+
+const char* pa_version(void) { return "libpa 0.1 gfx950"; }
+
+pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                      void* stream) {
+  const char* what = "pa_kv_write";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", what);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  return pa::launch_status(
+      pa::launch_kv_write(*layout, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
+      what);
+}
+
+pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+  const char* what = "pa_copy_blocks";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  const int64_t block_bytes = (int64_t)layout->block_size * layout->num_kv_heads *
+                              layout->head_dim * (layout->dtype == PA_BF16 ? 2 : 4);
+  if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
+  return pa::launch_status(
+      pa::launch_copy_blocks(*layout, k_pool, v_pool, pairs, num_pairs, stream), what);
+}
+
+static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, const void* q,
+                                  const void* k_pool, const void* v_pool,
+                                  const int32_t* block_tables, int32_t max_blocks,
+                                  const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, float scale, pa::DecodeArgs* a) {
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (pa_status st = pa::check_heads(layout, num_q_heads, what)) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs < 0", what);
+  if (max_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", what);
+  if ((int64_t)max_blocks * layout->block_size > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq*block_size overflows int32", what);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", what);
+  if (num_seqs > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens))
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  a->q = q;
+  a->k_pool = k_pool;
+  a->v_pool = v_pool;
+  a->block_tables = block_tables;
+  a->seq_lens = seq_lens;
+  a->cu_q_lens = nullptr;
+  a->out = nullptr;
+  a->part_o = nullptr;
+  a->part_lse = nullptr;
+  a->scale_log2 = scale * 1.44269504088896340736f;
+  a->num_seqs = num_seqs;
+  a->num_q_tokens = num_seqs;
+  a->num_q_heads = num_q_heads;
+  a->num_kv_heads = layout->num_kv_heads;
+  a->head_dim = layout->head_dim;
+  a->dtype = layout->dtype;
+  a->num_blocks = layout->num_blocks;
+  a->block_size = layout->block_size;
+  a->log2_bs = pa::log2i(layout->block_size);
+  a->max_blocks = max_blocks;
+  a->partition_size = 0;
+  a->max_partitions = 1;
+  a->waves_per_group = pa::waves_per_group(layout->num_kv_heads);
+  return PA_OK;
+}
+
+pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                    void* stream) {
+  const char* what = "pa_decode";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!out) return fail(PA_ERR_INVALID_ARG, "%s: out is NULL", what);
+  a.out = out;
+  return pa::launch_status(pa::launch_decode(a, false, stream), what);
+}
+
+pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,
+                          int32_t max_partitions, int32_t partition_size, const void* q,
+                          const int32_t* cu_q_lens, int32_t num_q_tokens, const void* k_pool,
+                          const void* v_pool, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                          int32_t num_q_heads, float scale, void* stream) {
+  const char* what = "pa_decode_split";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (num_q_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_q_tokens < 0", what);
+  if (!cu_q_lens && num_q_tokens != num_seqs)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: without cu_q_lens num_q_tokens (%d) must equal num_seqs (%d)", what,
+                num_q_tokens, num_seqs);
+  if (cu_q_lens && num_seqs == 0 && num_q_tokens != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: query tokens without sequences", what);
+  if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % layout->block_size != 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: partition_size %d must be a positive multiple of 16 and of block_size %d",
+                what, partition_size, layout->block_size);
+  if (max_partitions <= 0 || max_partitions > 65535)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_partitions must be in [1, 65535]", what);
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * layout->block_size)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: max_partitions*partition_size (%lld) < max_blocks_per_seq*block_size (%lld)",
+                what, (long long)max_partitions * partition_size,
+                (long long)max_blocks_per_seq * layout->block_size);
+  if (num_q_tokens == 0) return PA_OK;
+  if (!part_o || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: NULL partial buffer", what);
+  a.cu_q_lens = cu_q_lens;
+  a.num_q_tokens = num_q_tokens;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  return pa::launch_status(pa::launch_decode(a, true, stream), what);
+}
+
+pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const float* part_o,
+                    const float* part_lse, int32_t max_partitions, int32_t partition_size,
+                    const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim, void* stream) {
+  const char* what = "pa_reduce";
+  if (out_dtype != PA_F32 && out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: out_dtype %d is not PA_F32 or PA_BF16", what, out_dtype);
+  if (num_seqs < 0 || num_q_tokens < 0 || num_q_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: bad sizes", what);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {32, 64, 128, 256}", what, head_dim);
+  if (partition_size <= 0 || max_partitions <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: partition_size and max_partitions must be > 0", what);
+  if (!cu_q_lens && num_q_tokens != num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "%s: without cu_q_lens num_q_tokens must equal num_seqs", what);
+  if (num_q_tokens == 0) return PA_OK;
+  if (num_seqs == 0) return fail(PA_ERR_INVALID_ARG, "%s: query tokens without sequences", what);
+  if (!out || !part_o || !part_lse || !seq_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  pa::ReduceArgs a;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.cu_q_lens = cu_q_lens;
+  a.seq_lens = seq_lens;
+  a.out_dtype = out_dtype;
+  a.max_partitions = max_partitions;
+  a.partition_size = partition_size;
+  a.num_seqs = num_seqs;
+  a.num_q_tokens = num_q_tokens;
+  a.num_q_heads = num_q_heads;
+  a.head_dim = head_dim;
+  return pa::launch_status(pa::launch_reduce(a, stream), what);
+}
+
+}  // extern "C"

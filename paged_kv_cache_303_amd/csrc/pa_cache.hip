@@ -1,0 +1,163 @@
+// Slot-mapped cache writes, whole-block copies (copy-on-write) and the
+// log-sum-exp merge of split-sequence partitions, for gfx950.
+//
+// * kv_write ("19.2 KV Cache 系统化管理" §19.2.3, write_slot): token t's keys
+//   and values for all KV heads, one contiguous row of num_kv_heads*head_dim
+//   elements, go to pool row slot_mapping[t] (the flat slot
+//   physical*block_size + offset is exactly the pool row index).  One
+//   workgroup per token, 16-byte lanes.
+// * copy_blocks (same page, §19.2.2): pool[dst] = pool[src], K and V; a block
+//   is one contiguous span of block_size rows.  Workgroups stride over
+//   (pair, 16 KiB chunk) so a handful of pairs still fills the chip.
+// * reduce: the partitions of one query head are merged with weights
+//   exp(lse_p - L), L = log sum_p exp(lse_p) -- the online-softmax rescale of
+//   §19.2.3 applied once per partition.
+#include "pa_device.h"
+#include "pa_launch.h"
+
+namespace pa {
+namespace {
+
+__global__ __launch_bounds__(256) void kv_write_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                                       const char* __restrict__ kn,
+                                                       const char* __restrict__ vn,
+                                                       const int32_t* __restrict__ slots,
+                                                       int64_t row_bytes, int64_t num_rows) {
+  const int t = blockIdx.x;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_rows) return;
+  const int64_t n16 = row_bytes >> 4;
+  const uint4* sk = (const uint4*)(kn + (int64_t)t * row_bytes);
+  const uint4* sv = (const uint4*)(vn + (int64_t)t * row_bytes);
+  uint4* dk = (uint4*)(kp + s * row_bytes);
+  uint4* dv = (uint4*)(vp + s * row_bytes);
+  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
+    const uint4 a = sk[i];
+    const uint4 b = sv[i];
+    dk[i] = a;
+    dv[i] = b;
+  }
+}
+
+constexpr int64_t kCopyChunk = 16384;  // bytes per workgroup
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp, char* __restrict__ vp,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int64_t block_bytes, int32_t num_blocks,
+                                                          int64_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x % chunks_per_block;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t lo = chunk * kCopyChunk;
+  const int64_t hi = min(lo + kCopyChunk, block_bytes);
+  const int64_t n16 = (hi - lo) >> 4;
+  const uint4* sk = (const uint4*)(kp + src * block_bytes + lo);
+  const uint4* sv = (const uint4*)(vp + src * block_bytes + lo);
+  uint4* dk = (uint4*)(kp + dst * block_bytes + lo);
+  uint4* dv = (uint4*)(vp + dst * block_bytes + lo);
+  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
+    const uint4 a = sk[i];
+    const uint4 b = sv[i];
+    dk[i] = a;
+    dv[i] = b;
+  }
+}
+
+// One workgroup per query token; one wave per query head (strided).
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  const int j = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+
+  int b = j, q_first = j, q_len = 1;
+  if (a.cu_q_lens != nullptr) {
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_q_lens[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    q_first = a.cu_q_lens[b];
+    q_len = a.cu_q_lens[b + 1] - q_first;
+  }
+  const int len = max(a.seq_lens[b], 0);
+  const int key_end = len - q_len + (j - q_first) + 1;
+  int nparts = 0;
+  if (key_end > 0) nparts = q_len > 1 ? 1 : (key_end + a.partition_size - 1) / a.partition_size;
+  nparts = min(nparts, a.max_partitions);
+
+  const int D = a.head_dim;
+  for (int h = wave; h < a.num_q_heads; h += nwaves) {
+    const int64_t row = (int64_t)j * a.num_q_heads + h;
+    const float* lse = a.part_lse + row * a.max_partitions;
+    const float* po = a.part_o + row * a.max_partitions * D;
+    float m = -INFINITY;
+    for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
+    m = reduce_levels<0, 6>(m, OpMax());
+    float wsum = 0.f;
+    for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
+    wsum = reduce_levels<0, 6>(wsum, OpSum());
+    const float inv = nparts > 0 ? 1.f / wsum : 0.f;
+    for (int d0 = lane * 2; d0 < D; d0 += 2 * kWave) {
+      float o0 = 0.f, o1 = 0.f;
+      for (int p = 0; p < nparts; ++p) {
+        const float w = __expf(lse[p] - m);
+        const float2 v = *(const float2*)(po + (int64_t)p * D + d0);
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+      }
+      o0 *= inv;
+      o1 *= inv;
+      if (a.out_dtype == PA_BF16) {
+        uint32_t* out = (uint32_t*)((uint16_t*)a.out + row * D + d0);
+        *out = pack_bf16x2(o0, o1);
+      } else {
+        *(float2*)((float*)a.out + row * D + d0) = make_float2(o0, o1);
+      }
+    }
+    if (a.lse_out != nullptr && lane == 0)
+      a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
+  }
+}
+
+inline int64_t elt_size(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+
+}  // namespace
+
+pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
+                          const void* v_new, const int32_t* slots, int32_t num_tokens,
+                          void* stream) {
+  if (num_tokens == 0) return PA_OK;
+  const int64_t row_bytes = (int64_t)l.num_kv_heads * l.head_dim * elt_size(l.dtype);
+  const int64_t num_rows = (int64_t)l.num_blocks * l.block_size;
+  const int threads = row_bytes >= 4096 ? 256 : (row_bytes >= 2048 ? 128 : 64);
+  hipLaunchKernelGGL(kv_write_kernel, dim3(num_tokens), dim3(threads), 0, (hipStream_t)stream,
+                     (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, slots,
+                     row_bytes, num_rows);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_copy_blocks(const pa_kv_layout& l, void* k_pool, void* v_pool,
+                             const int32_t* pairs, int32_t num_pairs, void* stream) {
+  if (num_pairs == 0) return PA_OK;
+  const int64_t block_bytes =
+      (int64_t)l.block_size * l.num_kv_heads * l.head_dim * elt_size(l.dtype);
+  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)(num_pairs * chunks)), dim3(256), 0,
+                     (hipStream_t)stream, (char*)k_pool, (char*)v_pool, pairs, block_bytes,
+                     l.num_blocks, chunks);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_reduce(const ReduceArgs& a, void* stream) {
+  if (a.num_q_tokens == 0) return PA_OK;
+  const int waves = a.num_q_heads < 4 ? a.num_q_heads : 4;
+  hipLaunchKernelGGL(reduce_kernel, dim3(a.num_q_tokens), dim3(waves * kWave), 0,
+                     (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+}  // namespace pa

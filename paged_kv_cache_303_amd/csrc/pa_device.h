@@ -1,0 +1,123 @@
+// Device helpers for gfx950 (CDNA4, wave64): cross-lane reductions with DPP
+// and v_permlane{16,32}_swap, bfloat16 unpacking, dot2 and stores.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;
+
+__host__ __device__ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// ---------------------------------------------------------------------------
+// Cross-lane exchange by "level".  Level k pairs every lane with one lane of
+// the neighbouring aligned group of 2^k lanes:
+//   0: quad_perm [1,0,3,2]   (lane ^ 1)
+//   1: quad_perm [2,3,0,1]   (lane ^ 2)
+//   2: row_half_mirror        (i <-> 7-i inside each 8 lanes)
+//   3: row_mirror             (i <-> 15-i inside each 16-lane row)
+//   4: v_permlane16_swap      (rows 0<->1, 2<->3)
+//   5: v_permlane32_swap      (lanes 0-31 <-> 32-63)
+// Applying levels lo..hi-1 in order to a value that is already uniform
+// inside aligned groups of 2^lo lanes combines 2^(hi-lo) such groups, and the
+// result is uniform inside groups of 2^hi lanes: an all-reduce.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+struct OpSum {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+template <int LEVEL, class Op>
+__device__ __forceinline__ float level_step(float x, Op op) {
+  if constexpr (LEVEL == 0) {
+    return op(x, dpp_mov<0xB1>(x));
+  } else if constexpr (LEVEL == 1) {
+    return op(x, dpp_mov<0x4E>(x));
+  } else if constexpr (LEVEL == 2) {
+    return op(x, dpp_mov<0x141>(x));
+  } else if constexpr (LEVEL == 3) {
+    return op(x, dpp_mov<0x140>(x));
+  } else if constexpr (LEVEL == 4) {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  } else {
+    const unsigned u = __builtin_bit_cast(unsigned, x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+  }
+}
+
+template <int LO, int HI, class Op>
+__device__ __forceinline__ float reduce_levels(float x, Op op) {
+  if constexpr (LO < HI) {
+    x = level_step<LO>(x, op);
+    return reduce_levels<LO + 1, HI>(x, op);
+  } else {
+    return x;
+  }
+}
+
+// Cross-group reduction that keeps each lane's offset inside its group:
+// combines lanes i, i +- 2^LO, ... over the whole wave (levels LO..5) for
+// values that differ from lane to lane inside a group (e.g. one lane per
+// 16-byte chunk of a row).  Partners are exact: quad xor for levels 0-1, row
+// rotations by 4 and 8 for levels 2-3 (applied together they cover the four
+// quads of a row), the permlane swaps for levels 4-5.
+template <int LEVEL, class Op>
+__device__ __forceinline__ float aligned_step(float x, Op op) {
+  if constexpr (LEVEL == 2) {
+    return op(x, dpp_mov<0x124>(x));  // row_ror:4
+  } else if constexpr (LEVEL == 3) {
+    return op(x, dpp_mov<0x128>(x));  // row_ror:8
+  } else {
+    return level_step<LEVEL>(x, op);
+  }
+}
+
+template <int LO, class Op>
+__device__ __forceinline__ float reduce_groups(float x, Op op) {
+  if constexpr (LO < 6) {
+    x = aligned_step<LO>(x, op);
+    return reduce_groups<LO + 1>(x, op);
+  } else {
+    return x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 (bit patterns in uint16 / packed pairs in uint32)
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// a.lo*b.lo + a.hi*b.hi + c with fp32 accumulation (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// 2^x on the transcendental unit; exact 0 for x = -inf.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pa

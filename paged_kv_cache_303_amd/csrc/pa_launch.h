@@ -1,0 +1,62 @@
+// Internal launch interface between the C ABI entry points (pa_api.cpp) and
+// the kernel translation units.  Arguments here are already validated.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+struct DecodeArgs {
+  const void* q;               // [num_q_tokens, num_q_heads, head_dim]
+  const void* k_pool;          // [num_blocks, block_size, num_kv_heads, head_dim]
+  const void* v_pool;
+  const int32_t* block_tables; // [num_seqs, max_blocks]
+  const int32_t* seq_lens;     // [num_seqs]
+  const int32_t* cu_q_lens;    // [num_seqs + 1] or nullptr (one query per sequence)
+  void* out;                   // final output (pa_decode)
+  float* part_o;               // partial outputs (pa_decode_split)
+  float* part_lse;
+  float scale_log2;            // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;               // pa_dtype
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t log2_bs;
+  int32_t max_blocks;
+  int32_t partition_size;      // tokens per partition (split) or 0 (single pass)
+  int32_t max_partitions;
+  int32_t waves_per_group;     // KV heads (= waves) per workgroup
+};
+
+struct ReduceArgs {
+  void* out;
+  float* lse_out;
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* cu_q_lens;
+  const int32_t* seq_lens;
+  int32_t out_dtype;
+  int32_t max_partitions;
+  int32_t partition_size;
+  int32_t num_seqs;
+  int32_t num_q_tokens;
+  int32_t num_q_heads;
+  int32_t head_dim;
+};
+
+// Returns PA_OK, PA_ERR_UNSUPPORTED (no instance for the shape) or PA_ERR_HIP.
+pa_status launch_decode(const DecodeArgs& a, bool split, void* stream);
+pa_status launch_reduce(const ReduceArgs& a, void* stream);
+pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
+                          const void* v_new, const int32_t* slots, int32_t num_tokens,
+                          void* stream);
+pa_status launch_copy_blocks(const pa_kv_layout& l, void* k_pool, void* v_pool,
+                             const int32_t* pairs, int32_t num_pairs, void* stream);
+
+}  // namespace pa

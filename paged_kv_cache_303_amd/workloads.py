@@ -164,7 +164,7 @@ def worked_example(seed: int = 0, table: str = "random", dtype: str = F32) -> Wo
     rf, rq, rk, rv = _streams(seed, 4)
     free = None if table == "random" else np.arange(16, dtype=np.int32)
     return _decode_workload("worked_example", dtype, 16, 4, 8, 8, 32, [10],
-                            rf, rq, rk, rv, free_order=free, partition_size=4,
+                            rf, rq, rk, rv, free_order=free, partition_size=16,
                             info={"table": table})
 
 
