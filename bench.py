@@ -1,0 +1,276 @@
+"""Paged-decode throughput on one MI355X: effective KV GB/s and queries/s.
+
+Workload (the GQA decode batch): 256 sequences, 32 query / 8 KV heads, head
+dim 128, block size 16, bf16, lognormal lengths (median 1024, sigma 1,
+clipped to [16, 8192]), 65536-block pool with a permuted free list.  Inputs
+are seeded and synthetic (N(0,1) values); the context is written into the
+pools before timing.
+
+One step = the whole hot path for one decode round of the batch:
+  pa_kv_write   (one new token per sequence, through slot_mapping)
+  pa_decode_split (512-token partitions)
+  pa_reduce     (log-sum-exp merge, bf16 output)
+all on torch's current HIP stream, inputs resident in HBM.  W warm-up steps,
+then K timed steps bracketed by device synchronisation.
+
+Reported:
+  value          effective KV GB/s of the step = KV bytes / step time, with
+                 KV bytes = sum(len) * kv_heads * head_dim * 2 (K,V) * 2 B
+  roofline       the dominant kernel (pa_decode_split): its algorithmic bytes
+                 (KV + Q + block-table entries) over its average duration
+                 from HIP events around it on the launch stream, against
+                 8 TB/s; `traffic` is filled from rocprofv3 counters when
+                 they were taken for this kernel version (see --traffic)
+  cpu_baseline   the CPU oracle (float64 NumPy, single thread) timed on a
+                 bounded sample of the same queries (seeded order, ~15 s)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run pa_copy_blocks over this many MiB (counter calibration)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM bytes per launch measured with rocprofv3 counters")
+    ap.add_argument("--seed", type=int, default=2)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path; see the sharding notes of the design document.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_303_amd import build as pa_build
+    if not os.path.exists(pa_build.library_path()):
+        pa_build.build()
+    from paged_kv_cache_303_amd import binding, runner, workloads as wl
+
+    dev = torch.device("cuda", 0)
+    t0 = time.time()
+    w = wl.gqa_decode(seed=args.seed, partition_size=args.partition)
+    log(f"workload drawn in {time.time() - t0:.1f}s: {len(w.seq_lens)} seqs, "
+        f"{sum(w.seq_lens)} tokens, {w.kv_bytes / 1e9:.3f} GB of KV")
+
+    # ---- set up: context in the pools, tables on the device ---------------------
+    n_ctx = sum(w.seq_lens) - len(w.seq_lens)
+    w_ctx_ops = w.ops[: 2 * len(w.seq_lens)]  # new + context appends
+    st = runner.replay(_with_ops(w, w_ctx_ops), dev, poison=False)
+    pool = st["pool"]
+    handles = [st["handles"][s] for s in w.decode_seqs]
+    slots = np.concatenate([pool.append(h, 1)[0] for h in handles]).astype(np.int32)
+    seq_lens = np.array([pool.seq_len(h) for h in handles], dtype=np.int32)
+    assert seq_lens.tolist() == w.seq_lens
+    tables = pool.block_tables(handles, w.max_blocks)
+    k_tok = runner.to_device(w.k_tokens[n_ctx:], w.dtype, dev)
+    v_tok = runner.to_device(w.v_tokens[n_ctx:], w.dtype, dev)
+    slot_d = torch.from_numpy(slots).to(dev)
+    sl_d = torch.from_numpy(seq_lens).to(dev)
+    bt_d = torch.from_numpy(tables).to(dev)
+    q = runner.to_device(w.q, w.dtype, dev)
+    k_pool, v_pool = st["k_pool"], st["v_pool"]
+    maxp = binding.max_partitions_for(w.max_blocks, w.block_size, args.partition)
+    part_o = torch.empty((len(seq_lens), w.num_q_heads, maxp, w.head_dim), dtype=torch.float32,
+                         device=dev)
+    part_lse = torch.empty(part_o.shape[:3], dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        binding.kv_write(k_pool, v_pool, k_tok, v_tok, slot_d)
+        if ev is not None:
+            ev[0].record()
+        binding.decode_split(q, k_pool, v_pool, bt_d, sl_d, w.scale,
+                             partition_size=args.partition, part_o=part_o, part_lse=part_lse,
+                             max_partitions=maxp)
+        if ev is not None:
+            ev[1].record()
+        binding.reduce(part_o, part_lse, sl_d, args.partition, out_dtype=q.dtype, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole steps ------------------------------------------
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_step = 1e3 * t_total / args.steps
+    split_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+
+    # decode-only (split + reduce) timing, for context
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        binding.decode_split(q, k_pool, v_pool, bt_d, sl_d, w.scale,
+                             partition_size=args.partition, part_o=part_o, part_lse=part_lse,
+                             max_partitions=maxp)
+        binding.reduce(part_o, part_lse, sl_d, args.partition, out_dtype=q.dtype, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    decode_ms = e0.elapsed_time(e1) / args.steps
+
+    if args.calib_copy_mib > 0:
+        _calibration_copy(binding, k_pool, v_pool, args.calib_copy_mib, dev)
+
+    kv_bytes = w.kv_bytes
+    esize = 2
+    q_bytes = len(seq_lens) * w.num_q_heads * w.head_dim * esize
+    table_bytes = 4 * sum(-(-n // w.block_size) for n in w.seq_lens)
+    split_alg_bytes = kv_bytes + q_bytes + table_bytes
+    achieved = split_alg_bytes / (split_ms * 1e-3) / 1e9
+    traffic = _traffic(args.traffic)
+
+    result = {
+        "metric": "paged-decode effective KV GB/s (% of HBM peak) + queries/sec, GQA batch 256",
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "gqa_decode: batch 256, 32/8 heads, head_dim 128, block_size 16, bf16, "
+                        "lognormal lengths (median 1024, sigma 1.0, clip [16, 8192]), "
+                        "65536-block pool, kv_write of one token/seq + split decode + reduce",
+            "global_batch": len(seq_lens),
+            "total_tokens": int(sum(w.seq_lens)),
+            "max_len": int(max(w.seq_lens)),
+            "kv_bytes": int(kv_bytes),
+            "partition_size": args.partition,
+            "seed": args.seed,
+            "parallelism": "single GPU",
+        },
+        "pct_hbm_peak": round(100.0 * kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "queries_per_s": round(len(seq_lens) / (ms_step * 1e-3), 1),
+        "decode_only": {
+            "ms": round(decode_ms, 4),
+            "kv_GBps": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 1),
+            "queries_per_s": round(len(seq_lens) / (decode_ms * 1e-3), 1),
+        },
+        "roofline": {
+            "kernel": "pa_decode_split (decode_kernel<bf16,128,4,split>)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": int(split_alg_bytes),
+            "avg_launch_ms": round(split_ms, 4),
+        },
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = _cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def _with_ops(w, ops):
+    import copy
+    w2 = copy.copy(w)
+    w2.ops = ops
+    return w2
+
+
+def _calibration_copy(binding, k_pool, v_pool, mib, dev):
+    """pa_copy_blocks over `mib` MiB of K+V blocks: a plain copy of known size."""
+    import torch
+    block_bytes = k_pool[0].numel() * k_pool.element_size()
+    n = max(1, (mib << 20) // (2 * block_bytes))
+    n = min(n, k_pool.shape[0] // 2)
+    pairs = torch.stack([torch.arange(n), torch.arange(n) + k_pool.shape[0] // 2], 1)
+    pairs = pairs.to(torch.int32).to(dev)
+    binding.copy_blocks(k_pool, v_pool, pairs)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {n} block pairs, {2 * n * block_bytes} bytes read and written")
+
+
+def _traffic(path):
+    """HBM bytes per launch of the split kernel, from rocprofv3 counters, if current."""
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    from paged_kv_cache_303_amd import build as pa_build
+    if data.get("kernel_source_hash") != pa_build.source_hash():
+        return None
+    return data.get("bytes_per_launch")
+
+
+def _cpu_baseline(w, budget_s):
+    """The oracle as it stands, on a bounded, seeded sample of the same queries."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import runner as orun
+
+    t0 = time.time()
+    ost = orun.replay(w)
+    log(f"oracle replay (setup, untimed) {time.time() - t0:.1f}s")
+    order = np.random.default_rng(0).permutation(len(w.seq_lens)).tolist()
+    done = []
+    with threadpool_limits(limits=1):
+        start = time.perf_counter()
+        for j in order:
+            orun.attention(w, ost, tokens=[j])
+            done.append(j)
+            if time.perf_counter() - start >= budget_s:
+                break
+        elapsed = time.perf_counter() - start
+    kv = sum(w.seq_lens[j] for j in done) * w.num_kv_heads * w.head_dim * 2 * 2
+    return {
+        "value": round(kv / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "queries_per_s": round(len(done) / elapsed, 2),
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{len(done)} of {len(w.seq_lens)} decode queries (seeded order), "
+                  f"{sum(w.seq_lens[j] for j in done)} keys, {elapsed:.1f}s, float64 NumPy, "
+                  f"one thread",
+    }
+
+
+if __name__ == "__main__":
+    main()

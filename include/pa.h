@@ -36,8 +36,8 @@
  *   - Supported shapes: dtype PA_F32 or PA_BF16; head_dim 32, 64, 128 or
  *     256; block_size a power of two from 1 to 256; num_q_heads /
  *     num_kv_heads in {1, 2, 4, 8}.
- *   - Softmax scores are scale * dot(q, k); every workload passes
- *     1/sqrt(head_dim), the value the pages use.
+ *   - Softmax scores are scale * dot(q, k) with a finite scale > 0; every
+ *     workload passes 1/sqrt(head_dim), the value the pages use.
  */
 #ifndef PA_H_
 #define PA_H_

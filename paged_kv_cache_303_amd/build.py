@@ -31,13 +31,15 @@ COMMON = [
     "-mcode-object-version=5",
     "-Wall",
     "-Wno-unused-result",
+    "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 
 
 def library_path() -> str:
-    return os.path.join(PKG, "libpa.so")
+    """The library the binding loads: ``$PA_LIBRARY`` if set, else the in-tree build."""
+    return os.environ.get("PA_LIBRARY") or os.path.join(PKG, "libpa.so")
 
 
 def _hipcc() -> str:
@@ -51,9 +53,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, defines=(), build_dir=BUILD_DIR) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *[f"-D{d}" for d in defines], "-c", src, "-o", obj]
     if not src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,14 +68,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libpa.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str | None = None) -> str:
+    """Compile every source and link ``libpa.so``; returns its path.
+
+    ``defines`` (``NAME=VALUE`` strings) override compile-time tuning
+    parameters such as ``PA_TILE_TOKENS``; ``out`` places the library
+    elsewhere (the binding loads it when ``PA_LIBRARY`` names it).
+    """
+    build_dir = BUILD_DIR if not defines else os.path.join(
+        BUILD_DIR, "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     workers = min(len(srcs), max(1, (os.cpu_count() or 2) // 2), 8)
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    out = library_path()
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), srcs))
+    out = out or library_path()
     tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -81,6 +90,19 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, out)
     return out
+
+
+def source_hash() -> str:
+    """SHA-256 over the kernel sources and headers (ties measurements to a version)."""
+    import hashlib
+    h = hashlib.sha256()
+    files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    files.append(os.path.join(ROOT, "include", "pa.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -67,10 +67,14 @@ pa_status check_heads(const pa_kv_layout* l, int32_t num_q_heads, const char* wh
   return PA_OK;
 }
 
+#ifndef PA_WAVES_PER_GROUP
+#define PA_WAVES_PER_GROUP 4
+#endif
+
 // KV heads handled by one workgroup (one wave each): the largest divisor of
-// num_kv_heads that is at most 4.
+// num_kv_heads that is at most PA_WAVES_PER_GROUP.
 int32_t waves_per_group(int32_t num_kv_heads) {
-  for (int32_t w = 4; w > 1; --w)
+  for (int32_t w = PA_WAVES_PER_GROUP; w > 1; --w)
     if (num_kv_heads % w == 0) return w;
   return 1;
 }
@@ -132,7 +136,8 @@ static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, 
   if (max_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", what);
   if ((int64_t)max_blocks * layout->block_size > (int64_t)INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq*block_size overflows int32", what);
-  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", what);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "%s: scale must be finite and > 0", what);
   if (num_seqs > 0 && (!q || !k_pool || !v_pool || !block_tables || !seq_lens))
     return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
   a->q = q;

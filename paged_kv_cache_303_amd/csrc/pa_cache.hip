@@ -65,12 +65,14 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp,
   }
 }
 
-// One workgroup per query token; one wave per query head (strided).
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+// One wave per (query token, query head); kReduceWaves heads per workgroup.
+constexpr int kReduceWaves = 4;
+
+__global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs a) {
   const int j = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int nwaves = blockDim.x / kWave;
+  const int h = blockIdx.y * kReduceWaves + threadIdx.x / kWave;
+  if (h >= a.num_q_heads) return;
 
   int b = j, q_first = j, q_len = 1;
   if (a.cu_q_lens != nullptr) {
@@ -90,37 +92,39 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
   nparts = min(nparts, a.max_partitions);
 
   const int D = a.head_dim;
-  for (int h = wave; h < a.num_q_heads; h += nwaves) {
-    const int64_t row = (int64_t)j * a.num_q_heads + h;
-    const float* lse = a.part_lse + row * a.max_partitions;
-    const float* po = a.part_o + row * a.max_partitions * D;
-    float m = -INFINITY;
-    for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
-    m = reduce_levels<0, 6>(m, OpMax());
-    float wsum = 0.f;
-    for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
-    wsum = reduce_levels<0, 6>(wsum, OpSum());
-    const float inv = nparts > 0 ? 1.f / wsum : 0.f;
-    for (int d0 = lane * 2; d0 < D; d0 += 2 * kWave) {
-      float o0 = 0.f, o1 = 0.f;
-      for (int p = 0; p < nparts; ++p) {
-        const float w = __expf(lse[p] - m);
-        const float2 v = *(const float2*)(po + (int64_t)p * D + d0);
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
-      }
-      o0 *= inv;
-      o1 *= inv;
-      if (a.out_dtype == PA_BF16) {
-        uint32_t* out = (uint32_t*)((uint16_t*)a.out + row * D + d0);
-        *out = pack_bf16x2(o0, o1);
-      } else {
-        *(float2*)((float*)a.out + row * D + d0) = make_float2(o0, o1);
-      }
+  const int64_t row = (int64_t)j * a.num_q_heads + h;
+  const float* lse = a.part_lse + row * a.max_partitions;
+  const float* po = a.part_o + row * a.max_partitions * D;
+  float m = -INFINITY;
+  for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
+  m = reduce_levels<0, 6>(m, OpMax());
+  float wsum = 0.f;
+  for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
+  wsum = reduce_levels<0, 6>(wsum, OpSum());
+  const float inv = nparts > 0 ? 1.f / wsum : 0.f;
+
+  for (int d = lane; d < D; d += kWave) {
+    float o = 0.f;
+    int p = 0;
+    for (; p + 4 <= nparts; p += 4) {  // four partitions in flight
+      const float v0 = po[(int64_t)(p + 0) * D + d];
+      const float v1 = po[(int64_t)(p + 1) * D + d];
+      const float v2 = po[(int64_t)(p + 2) * D + d];
+      const float v3 = po[(int64_t)(p + 3) * D + d];
+      o = fmaf(__expf(lse[p + 0] - m), v0, o);
+      o = fmaf(__expf(lse[p + 1] - m), v1, o);
+      o = fmaf(__expf(lse[p + 2] - m), v2, o);
+      o = fmaf(__expf(lse[p + 3] - m), v3, o);
     }
-    if (a.lse_out != nullptr && lane == 0)
-      a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
+    for (; p < nparts; ++p) o = fmaf(__expf(lse[p] - m), po[(int64_t)p * D + d], o);
+    o *= inv;
+    if (a.out_dtype == PA_BF16)
+      ((__bf16*)a.out)[row * D + d] = (__bf16)o;
+    else
+      ((float*)a.out)[row * D + d] = o;
   }
+  if (a.lse_out != nullptr && lane == 0)
+    a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
 }
 
 inline int64_t elt_size(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
@@ -154,9 +158,8 @@ pa_status launch_copy_blocks(const pa_kv_layout& l, void* k_pool, void* v_pool,
 
 pa_status launch_reduce(const ReduceArgs& a, void* stream) {
   if (a.num_q_tokens == 0) return PA_OK;
-  const int waves = a.num_q_heads < 4 ? a.num_q_heads : 4;
-  hipLaunchKernelGGL(reduce_kernel, dim3(a.num_q_tokens), dim3(waves * kWave), 0,
-                     (hipStream_t)stream, a);
+  const dim3 grid(a.num_q_tokens, (a.num_q_heads + kReduceWaves - 1) / kReduceWaves);
+  hipLaunchKernelGGL(reduce_kernel, grid, dim3(kReduceWaves * kWave), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

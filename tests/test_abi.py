@@ -77,6 +77,8 @@ def test_decode_argument_validation(built_library):
     assert lib.pa_decode(ctypes.byref(lay), nul, d, d, d, d, 4, d, 1, 32, 0.1, None) == 1
     assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 0, d, 1, 32, 0.1, None) == 1
     assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, float("nan"), None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, -0.5, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, 0.0, None) == 1
     assert lib.pa_decode(None, d, d, d, d, d, 4, d, 1, 32, 0.1, None) == 1
     # zero sequences is a no-op
     assert lib.pa_decode(ctypes.byref(lay), nul, nul, d, d, nul, 4, nul, 0, 32, 0.1, None) == 0
