@@ -8,19 +8,21 @@ pools before timing.
 
 One step = the whole hot path for one decode round of the batch:
   pa_kv_write   (one new token per sequence, through slot_mapping)
-  pa_decode_split (512-token partitions)
-  pa_reduce     (log-sum-exp merge, bf16 output)
+  pa_decode     (balanced path: equal slices of the batch's work, one per
+                 resident workgroup, then the merge of cut sequences)
 all on torch's current HIP stream, inputs resident in HBM.  W warm-up steps,
-then K timed steps bracketed by device synchronisation.
+then K timed steps bracketed by device synchronisation.  The fixed-partition
+path (pa_decode_split + pa_reduce) is timed too, for comparison.
 
 Reported:
   value          effective KV GB/s of the step = KV bytes / step time, with
                  KV bytes = sum(len) * kv_heads * head_dim * 2 (K,V) * 2 B
-  roofline       the dominant kernel (pa_decode_split): its algorithmic bytes
-                 (KV + Q + block-table entries) over its average duration
-                 from HIP events around it on the launch stream, against
-                 8 TB/s; `traffic` is filled from rocprofv3 counters when
-                 they were taken for this kernel version (see --traffic)
+  roofline       the dominant call (pa_decode: the streaming kernel plus its
+                 small merge kernel): algorithmic bytes (KV + Q + O +
+                 block-table entries) over its average duration from HIP
+                 events around it on the launch stream, against 8 TB/s;
+                 `traffic` is filled from rocprofv3 counters when they were
+                 taken for this kernel version (see --traffic)
   cpu_baseline   the CPU oracle (float64 NumPy, single thread) timed on a
                  bounded sample of the same queries (seeded order, ~15 s)
 
@@ -105,18 +107,16 @@ def main():
                          device=dev)
     part_lse = torch.empty(part_o.shape[:3], dtype=torch.float32, device=dev)
     out = torch.empty_like(q)
+    ws = binding.decode_workspace(k_pool, len(seq_lens), w.num_q_heads)
     torch.cuda.synchronize()
 
     def step(ev=None):
         binding.kv_write(k_pool, v_pool, k_tok, v_tok, slot_d)
         if ev is not None:
             ev[0].record()
-        binding.decode_split(q, k_pool, v_pool, bt_d, sl_d, w.scale,
-                             partition_size=args.partition, part_o=part_o, part_lse=part_lse,
-                             max_partitions=maxp)
+        binding.decode(q, k_pool, v_pool, bt_d, sl_d, w.scale, out=out, workspace=ws)
         if ev is not None:
             ev[1].record()
-        binding.reduce(part_o, part_lse, sl_d, args.partition, out_dtype=q.dtype, out=out)
 
     for _ in range(args.warmup):
         step()
@@ -132,9 +132,9 @@ def main():
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_step = 1e3 * t_total / args.steps
-    split_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
 
-    # decode-only (split + reduce) timing, for context
+    # the fixed-partition path (split + reduce), for context
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
@@ -144,7 +144,7 @@ def main():
         binding.reduce(part_o, part_lse, sl_d, args.partition, out_dtype=q.dtype, out=out)
     e1.record()
     torch.cuda.synchronize()
-    decode_ms = e0.elapsed_time(e1) / args.steps
+    split_ms = e0.elapsed_time(e1) / args.steps
 
     if args.calib_copy_mib > 0:
         _calibration_copy(binding, k_pool, v_pool, args.calib_copy_mib, dev)
@@ -153,8 +153,8 @@ def main():
     esize = 2
     q_bytes = len(seq_lens) * w.num_q_heads * w.head_dim * esize
     table_bytes = 4 * sum(-(-n // w.block_size) for n in w.seq_lens)
-    split_alg_bytes = kv_bytes + q_bytes + table_bytes
-    achieved = split_alg_bytes / (split_ms * 1e-3) / 1e9
+    alg_bytes = kv_bytes + 2 * q_bytes + table_bytes  # K, V, Q in, O out, table
+    achieved = alg_bytes / (decode_ms * 1e-3) / 1e9
     traffic = _traffic(args.traffic)
 
     result = {
@@ -173,12 +173,12 @@ def main():
         "config": {
             "workload": "gqa_decode: batch 256, 32/8 heads, head_dim 128, block_size 16, bf16, "
                         "lognormal lengths (median 1024, sigma 1.0, clip [16, 8192]), "
-                        "65536-block pool, kv_write of one token/seq + split decode + reduce",
+                        "65536-block pool, kv_write of one token/seq + balanced pa_decode",
             "global_batch": len(seq_lens),
             "total_tokens": int(sum(w.seq_lens)),
             "max_len": int(max(w.seq_lens)),
             "kv_bytes": int(kv_bytes),
-            "partition_size": args.partition,
+            "decode_slices": _slices(ws, len(seq_lens), w.num_q_heads, w.head_dim),
             "seed": args.seed,
             "parallelism": "single GPU",
         },
@@ -189,21 +189,36 @@ def main():
             "kv_GBps": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 1),
             "queries_per_s": round(len(seq_lens) / (decode_ms * 1e-3), 1),
         },
+        "split_path": {
+            "partition_size": args.partition,
+            "ms": round(split_ms, 4),
+            "kv_GBps": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1),
+        },
         "roofline": {
-            "kernel": "pa_decode_split (decode_kernel<bf16,128,4,split>)",
+            "kernel": "pa_decode (decode_stream_kernel<bf16,128,4> + stream_fixup_kernel)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
-            "alg_bytes_per_launch": int(split_alg_bytes),
-            "avg_launch_ms": round(split_ms, 4),
+            "alg_bytes_per_launch": int(alg_bytes),
+            "avg_launch_ms": round(decode_ms, 4),
         },
     }
     if args.cpu_budget > 0:
         result["cpu_baseline"] = _cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def _slices(ws, num_seqs, hq, d):
+    """Slices of the balanced decode, from its workspace size (layout of pa_decode)."""
+    if ws is None:
+        return None
+    a256 = lambda x: (x + 255) // 256 * 256
+    per_slice = 2 * hq * d * 4 + 2 * hq * 4
+    rest = ws.numel() - a256((num_seqs + 1) * 4)
+    return int(rest // per_slice)
 
 
 def _with_ops(w, ops):

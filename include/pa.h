@@ -102,20 +102,34 @@ pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool,
 pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
                          const int32_t* pairs, int32_t num_pairs, void* stream);
 
-/* Single-pass paged decode ("19.2 KV Cache 系统化管理" §19.2.3,
- * paged_attention): one query token per sequence, at position seq_len-1,
- * attending to keys 0 .. seq_len-1 of its own table.
+/* Paged decode ("19.2 KV Cache 系统化管理" §19.2.3, paged_attention): one
+ * query token per sequence, at position seq_len-1, attending to keys
+ * 0 .. seq_len-1 of its own table; returns the final output in one call.
  *   q, out       : [num_seqs, num_q_heads, head_dim], pool dtype; query head h
  *                  reads KV head h / (num_q_heads/num_kv_heads)
  *   block_tables : device int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens     : device int32 [num_seqs] (tokens in the cache, including
  *                  this step's token); seq_len 0 gives a zero row
+ *   workspace    : NULL, or caller-owned device memory of workspace_bytes >=
+ *                  pa_decode_workspace_size(...), 256-byte aligned.  With a
+ *                  workspace the batch's work is split into equal slices,
+ *                  one per workgroup the device holds at once (balanced over
+ *                  uneven lengths; queries cut by a slice boundary are merged
+ *                  by a second kernel in the same call).  Without one, each
+ *                  (sequence, KV-head group) is one workgroup.  Calls sharing
+ *                  a workspace must be ordered on one stream.
  * Accumulation is fp32; bf16 outputs are rounded to nearest even. */
 pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q,
                     const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                    float scale, void* stream);
+                    float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace pa_decode uses for these sizes on the current device
+ * (0: the balanced path does not apply, e.g. more than 4096 sequences, and
+ * the workspace is ignored). */
+pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
+                                   int32_t num_q_heads, size_t* bytes);
 
 /* Split-sequence paged attention, first pass.  The keys a query sees are cut
  * into partitions of `partition_size` tokens (partition p = keys

@@ -54,7 +54,9 @@ _SIGNATURES = {
     "pa_version": (ctypes.c_char_p, []),
     "pa_kv_write": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p]),
     "pa_copy_blocks": (_i32, [_LAYOUT, _p, _p, _p, _i32, _p]),
-    "pa_decode": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p]),
+    "pa_decode": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p,
+                         ctypes.c_size_t, _p]),
+    "pa_decode_workspace_size": (_i32, [_LAYOUT, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pa_decode_split": (_i32, [_LAYOUT, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p,
                                _i32, _i32, _f32, _p]),
     "pa_reduce": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]),
@@ -176,8 +178,30 @@ def _tables(block_tables, seq_lens, num_seqs):
             _dev(seq_lens, "seq_lens", torch.int32))
 
 
-def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None):
-    """``pa_decode``: one query per sequence, single pass.  Returns ``out``."""
+def decode_workspace_size(k_pool, num_seqs: int, num_q_heads: int) -> int:
+    """``pa_decode_workspace_size``: bytes of the balanced path's workspace."""
+    lay = layout_of(k_pool)
+    n = ctypes.c_size_t()
+    _check(lib().pa_decode_workspace_size(ctypes.byref(lay), int(num_seqs), int(num_q_heads),
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def decode_workspace(k_pool, num_seqs: int, num_q_heads: int):
+    """A device workspace for ``decode`` (None when the balanced path does not apply)."""
+    n = decode_workspace_size(k_pool, num_seqs, num_q_heads)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=k_pool.device)
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, workspace=None):
+    """``pa_decode``: one query per sequence.  Returns ``out``.
+
+    ``workspace`` (a uint8 device tensor from :func:`decode_workspace`)
+    selects the load-balanced path; without it every (sequence, KV-head
+    group) is one workgroup.
+    """
     lay, kp, vp = _pools(k_pool, v_pool)
     if q.dim() != 3 or q.shape[2] != lay.head_dim:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
@@ -187,9 +211,14 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None):
         out = torch.empty_like(q)
     elif out.shape != q.shape:
         raise ValueError("out must have q's shape")
+    ws = ctypes.c_void_p(0)
+    ws_bytes = 0
+    if workspace is not None:
+        ws = _dev(workspace, "workspace", torch.uint8)
+        ws_bytes = workspace.numel()
     _check(lib().pa_decode(ctypes.byref(lay), _dev(out, "out", k_pool.dtype),
                            _dev(q, "q", k_pool.dtype), kp, vp, bt, mb, sl, b, hq, float(scale),
-                           _stream()))
+                           ws, ws_bytes, _stream()))
     return out
 
 

@@ -26,7 +26,7 @@ ARCH = "gfx950"
 COMMON = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-mcode-object-version=5",
     "-Wall",

@@ -68,7 +68,7 @@ pa_status check_heads(const pa_kv_layout* l, int32_t num_q_heads, const char* wh
 }
 
 #ifndef PA_WAVES_PER_GROUP
-#define PA_WAVES_PER_GROUP 4
+#define PA_WAVES_PER_GROUP 2
 #endif
 
 // KV heads handled by one workgroup (one wave each): the largest divisor of
@@ -89,41 +89,6 @@ pa_status launch_status(pa_status st, const char* what) {
 }  // namespace pa
 
 using pa::fail;
-
-extern "C" {
-
-const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
-
-const char* pa_version(void) { return "libpa 0.1 gfx950"; }
-
-pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool, const void* k_new,
-                      const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
-                      void* stream) {
-  const char* what = "pa_kv_write";
-  if (pa_status st = pa::check_layout(layout, what)) return st;
-  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", what);
-  if (num_tokens == 0) return PA_OK;
-  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
-    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
-  return pa::launch_status(
-      pa::launch_kv_write(*layout, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
-      what);
-}
-
-pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
-                         const int32_t* pairs, int32_t num_pairs, void* stream) {
-  const char* what = "pa_copy_blocks";
-  if (pa_status st = pa::check_layout(layout, what)) return st;
-  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
-  if (num_pairs == 0) return PA_OK;
-  if (!k_pool || !v_pool || !pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
-  const int64_t block_bytes = (int64_t)layout->block_size * layout->num_kv_heads *
-                              layout->head_dim * (layout->dtype == PA_BF16 ? 2 : 4);
-  if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
-    return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
-  return pa::launch_status(
-      pa::launch_copy_blocks(*layout, k_pool, v_pool, pairs, num_pairs, stream), what);
-}
 
 static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, const void* q,
                                   const void* k_pool, const void* v_pool,
@@ -166,10 +131,89 @@ static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, 
   return PA_OK;
 }
 
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct StreamLayout {
+  int32_t slices = 0;
+  size_t o_bytes = 0, lse_bytes = 0, cum_bytes = 0;
+  size_t total() const { return o_bytes + lse_bytes + cum_bytes; }
+};
+
+// Workspace of the balanced path for these arguments (slices = 0: the batch
+// is too large for it and the grid kernel runs instead).
+pa_status stream_layout(const pa::DecodeArgs& a, StreamLayout* sl) {
+  *sl = StreamLayout();
+  if (a.num_seqs <= 0 || a.num_seqs > pa::kStreamMaxSeqs) return PA_OK;
+  int32_t slices = 0;
+  const pa_status st = pa::stream_slices(a, &slices);
+  if (st != PA_OK) return st;
+  sl->slices = slices;
+  sl->o_bytes = align256((size_t)slices * 2 * a.num_q_heads * a.head_dim * sizeof(float));
+  sl->lse_bytes = align256((size_t)slices * 2 * a.num_q_heads * sizeof(float));
+  sl->cum_bytes = align256((size_t)(a.num_seqs + 1) * sizeof(int32_t));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return pa::g_last_error.c_str(); }
+
+const char* pa_version(void) { return "libpa 0.1 gfx950"; }
+
+pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int32_t* slot_mapping, int32_t num_tokens,
+                      void* stream) {
+  const char* what = "pa_kv_write";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", what);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  return pa::launch_status(
+      pa::launch_kv_write(*layout, k_pool, v_pool, k_new, v_new, slot_mapping, num_tokens, stream),
+      what);
+}
+
+pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+  const char* what = "pa_copy_blocks";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  const int64_t block_bytes = (int64_t)layout->block_size * layout->num_kv_heads *
+                              layout->head_dim * (layout->dtype == PA_BF16 ? 2 : 4);
+  if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
+  return pa::launch_status(
+      pa::launch_copy_blocks(*layout, k_pool, v_pool, pairs, num_pairs, stream), what);
+}
+
+pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
+                                   int32_t num_q_heads, size_t* bytes) {
+  const char* what = "pa_decode_workspace_size";
+  if (!bytes) return fail(PA_ERR_INVALID_ARG, "%s: bytes is NULL", what);
+  *bytes = 0;
+  pa::DecodeArgs a;
+  const void* dummy = (const void*)16;
+  if (pa_status st = fill_decode_args(what, layout, dummy, dummy, dummy, (const int32_t*)dummy, 1,
+                                      (const int32_t*)dummy, num_seqs, num_q_heads, 1.f, &a))
+    return st;
+  StreamLayout sl;
+  if (pa_status st = stream_layout(a, &sl))
+    return fail(st, "%s: cannot query the device occupancy", what);
+  *bytes = sl.total();
+  return PA_OK;
+}
+
 pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const void* k_pool,
                     const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                    void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream) {
   const char* what = "pa_decode";
   pa::DecodeArgs a;
   if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
@@ -179,6 +223,25 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const 
   if (num_seqs == 0) return PA_OK;
   if (!out) return fail(PA_ERR_INVALID_ARG, "%s: out is NULL", what);
   a.out = out;
+  if (workspace != nullptr) {
+    StreamLayout sl;
+    if (pa_status st = stream_layout(a, &sl))
+      return fail(st, "%s: cannot query the device occupancy", what);
+    if (sl.slices > 0) {
+      if (workspace_bytes < sl.total())
+        return fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < %zu needed", what,
+                    workspace_bytes, sl.total());
+      if (((uintptr_t)workspace & 255) != 0)
+        return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", what);
+      char* ws = (char*)workspace;
+      pa::StreamArgs s;
+      s.part_o = (float*)ws;
+      s.part_lse = (float*)(ws + sl.o_bytes);
+      s.cum = (int32_t*)(ws + sl.o_bytes + sl.lse_bytes);
+      s.num_slices = sl.slices;
+      return pa::launch_status(pa::launch_decode_stream(a, s, stream), what);
+    }
+  }
   return pa::launch_status(pa::launch_decode(a, false, stream), what);
 }
 

@@ -1,33 +1,40 @@
 // Paged decode attention on gfx950: block-table gather, QK, online softmax,
-// PV -- single pass (final output) or one partition per workgroup (partials
-// for the log-sum-exp reduce).
+// PV.  Three kernels share one per-wave tile machinery (WaveCtx):
+//   * decode_kernel        grid of (query token, KV-head group, partition):
+//                          single pass (final output) or one fixed partition
+//                          per workgroup (partials for the log-sum-exp reduce)
+//   * decode_stream_kernel persistent and load-balanced: every workgroup takes
+//                          an equal, contiguous slice of all (sequence, tile)
+//                          work, finishes the sequences that lie inside its
+//                          slice and leaves (o, lse) partials for cut ones
+//   * stream_fixup_kernel  merges the cut sequences' partials; zero rows for
+//                          sequences without keys
 //
 // What it computes ("19.2 KV Cache 系统化管理" §19.2.3, paged_attention): for
 // one query token, walk the request's keys in logical order through its block
 // table (logical block t / block_size -> physical block, row t % block_size;
 // "LLM 推理引擎的内存管理与调度" §3), and fold them into a running maximum m,
 // a running sum l of exp(s - m) and a running weighted sum of values, both
-// rescaled by exp(m_old - m_new) whenever the maximum grows; divide at the end.
-// The unit folded at once is a tile of 16 tokens instead of one block.
+// rescaled by exp(m_old - m_new) when the maximum grows; divide at the end.
+// The unit folded at once is a tile of TT tokens instead of one block.
 //
-// Work decomposition (one workgroup = one query token x a group of KV heads x
-// one partition; one wave per KV head):
+// Per wave (one KV head):
 //   * The wave serves the G = num_q_heads/num_kv_heads query heads that share
-//     its KV head, so every K/V byte is read once per KV head (grouped-query
-//     attention) and used G times.
+//     its KV head, so every K/V byte is read once per KV head and used G times.
 //   * Loads are 16 bytes per lane and row-contiguous: a token row of one KV
-//     head (head_dim elements) is read by LPR = head_dim*elt/16 neighbouring
-//     lanes, TPI = 64/LPR rows per load instruction, NI instructions per tile.
-//   * QK: each lane takes partial dot products over its 16-byte chunk for the
-//     G heads (v_dot2_f32_bf16 for bfloat16) and the LPR lanes of a row are
-//     summed with DPP row operations -- no LDS.  After that every lane holds
-//     the full scores of its own tokens, exactly the tokens whose V chunk it
-//     loaded, so PV needs no exchange either.
-//   * Softmax runs in the log2 domain (scores carry scale*log2(e)); the tile
-//     maximum crosses token groups with DPP / v_permlane{16,32}_swap.
-//   * Masked tokens (past the partition end) load a clamped in-range row and
-//     get probability exactly 0, so the NaN-poisoned tails of partly filled
-//     blocks never reach the sums.
+//     head is read by LPR neighbouring lanes (CPL chunks each), TPI rows per
+//     load instruction, NI instructions per tile.
+//   * QK: partial dot products over the lane's chunks (v_dot2_f32_bf16 for
+//     bfloat16), summed over the LPR lanes of a row with DPP row operations;
+//     every lane then holds the full scores of the tokens whose V chunks it
+//     loaded, so PV needs no exchange.
+//   * Softmax in the log2 domain, lazily rescaled; the tile maximum crosses
+//     token groups with DPP / v_permlane{16,32}_swap.
+//   * Software pipeline: the next tile's loads are in flight while the current
+//     tile is computed.  Rows past a range's end are clamped to its last row
+//     and get probability exactly 0, so NaN-poisoned tails never reach sums.
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_launch.h"
 
@@ -47,14 +54,6 @@ struct Elt<uint16_t> {  // bfloat16 bit patterns
   static constexpr int kVec = 8;
 };
 
-// Lane layout for (element type, head_dim, query heads per KV head):
-//   CPL  16-byte chunks of a row per lane (2 halves the row reduction and the
-//        redundant exponentials; 1 when G is large, to bound accumulators)
-//   LPR  lanes per token row, TPI rows per load instruction
-//   NI   load instructions (of CPL chunks each) per tile, TT tokens per tile
-#ifndef PA_GROUP_MAJOR
-#define PA_GROUP_MAJOR 0  // 1: KV-head groups vary fastest in the grid
-#endif
 #ifndef PA_TILE_TOKENS
 #define PA_TILE_TOKENS 32  // target tokens per tile (per wave, per KV head)
 #endif
@@ -62,6 +61,11 @@ struct Elt<uint16_t> {  // bfloat16 bit patterns
 #define PA_MAX_TILE_LOADS 8  // 16-byte loads per lane per tile (K or V), hot shapes
 #endif
 
+// Lane layout for (element type, head_dim, query heads per KV head):
+//   CPL  16-byte chunks of a row per lane (2 halves the row reduction and the
+//        redundant exponentials; 1 when G is large, to bound accumulators)
+//   LPR  lanes per token row, TPI rows per load instruction
+//   NI   load instructions (of CPL chunks each) per tile, TT tokens per tile
 template <typename T, int D, int G, bool UNIFORM = true>
 struct Shape {
   static constexpr int VEC = Elt<T>::kVec;
@@ -70,16 +74,17 @@ struct Shape {
   static constexpr int LPR = CHUNKS / CPL;
   static constexpr int TPI = kWave / LPR;
   // Loads per lane per tile (K or V; two tiles are in registers at a time):
-  // the bf16 shapes with small G get the full budget, the others half of it
-  // so that accumulators and both tiles stay in 256 VGPRs without spilling.
+  // the bf16 shapes with small G get the full budget, the others less, so
+  // that accumulators and both tiles stay in 256 VGPRs without spilling.
   static constexpr int MAX_LOADS =
       (sizeof(T) == 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
       : (G >= 8 ? PA_MAX_TILE_LOADS / 4 : PA_MAX_TILE_LOADS / 2);
   static constexpr int NI0 = (PA_TILE_TOKENS / TPI) < 1 ? 1 : (PA_TILE_TOKENS / TPI);
   static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
   static constexpr int TT = NI * TPI;
-  // Tiles start at multiples of 16 plus multiples of TT, so every load
-  // instruction starts on a multiple of TPI (needed by the UNIFORM lookup).
+  // Ranges start at multiples of 16 (partitions) or of TT (slices), plus
+  // multiples of TT, so every load instruction starts on a multiple of TPI
+  // (needed by the UNIFORM lookup).
   static_assert(LPR * CPL * VEC == D && LPR <= kWave && (16 % TPI) == 0 && NI >= 1,
                 "unsupported lane layout");
 };
@@ -89,142 +94,102 @@ struct Shape {
 // 2^kLazy and the O(G*D) rescale of the accumulators is rare.  The result
 // is independent of m up to rounding (acc and l carry the same factor).
 constexpr float kLazy = 8.0f;
+constexpr float kLn2 = 0.69314718055994530942f;
 
+// Per-wave state and tile machinery for one KV head and its G query heads.
 // UNIFORM: the rows of one load instruction always share a block (the block
 // size is a multiple of TPI), so block-table entries are wave-uniform scalar
 // loads; otherwise every lane looks its block up.
-template <typename T, int D, int G, bool SPLIT, bool UNIFORM>
-__global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(DecodeArgs a) {
+template <typename T, int D, int G, bool UNIFORM>
+struct WaveCtx {
   using S = Shape<T, D, G, UNIFORM>;
-  constexpr int VEC = S::VEC;
-  constexpr int CPL = S::CPL;
-  constexpr int LPR = S::LPR;
-  constexpr int LOG_LPR = ilog2(LPR);
-  constexpr int TPI = S::TPI;
-  constexpr int NI = S::NI;
-  constexpr int TT = S::TT;
-  constexpr bool BF16 = sizeof(T) == 2;
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int tg = lane / LPR;  // which row of a load instruction
-  const int c = lane % LPR;   // first 16-byte chunk of this lane (then c + LPR, ...)
-#if PA_GROUP_MAJOR
-  const int j = blockIdx.y;   // query token
-  const int kvh = blockIdx.x * a.waves_per_group + wave;
-#else
-  const int j = blockIdx.x;   // query token
-  const int kvh = blockIdx.y * a.waves_per_group + wave;
-#endif
-  // Partitions run last-first so the long sequences' tails start early.
-  const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
-
-  // --- query token -> sequence, position, key range -------------------------
-  int b = j, q_first = j, q_len = 1;
-  if (a.cu_q_lens != nullptr) {
-    int lo = 0, hi = a.num_seqs - 1;  // last b with cu[b] <= j
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cu_q_lens[mid] <= j) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-    q_first = a.cu_q_lens[b];
-    q_len = a.cu_q_lens[b + 1] - q_first;
-  }
-  const int cap = a.max_blocks << a.log2_bs;
-  const int len = min(max(a.seq_lens[b], 0), cap);
-  const int key_end = len - q_len + (j - q_first) + 1;  // keys 0 .. position
-  int start = 0, end = key_end;
-  if constexpr (SPLIT) {
-    if (q_len > 1) {
-      if (part != 0) return;  // multi-query sequences: one partition
-    } else {
-      start = part * a.partition_size;
-      end = min(key_end, start + a.partition_size);
-    }
-    if (start >= end) return;  // this partition holds no key
-  }
-  const int h0 = kvh * G;
-  if constexpr (!SPLIT) {
-    if (end <= 0) {  // no key: zero row
-      if (tg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int k = 0; k < CPL; ++k)
-            *(uint4*)((T*)a.out + ((int64_t)j * a.num_q_heads + h0 + g) * D +
-                      (c + k * LPR) * VEC) = make_uint4(0, 0, 0, 0);
-      }
-      return;
-    }
-  }
-
-  // --- query: this lane's chunks of each of the G heads ------------------------
-  // Scores are kept unscaled; scale*log2(e) is applied inside the exponent's
-  // fma (bf16) or folded into the fp32 query.  Requires scale > 0.
-  const T* qrow = (const T*)a.q + ((int64_t)j * a.num_q_heads + h0) * D;
-  uint4 qraw[G][CPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int k = 0; k < CPL; ++k)
-      qraw[g][k] = *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC);
-  float qf[G][CPL][4];
-  if constexpr (!BF16) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        qf[g][k][0] = __uint_as_float(qraw[g][k].x) * a.scale_log2;
-        qf[g][k][1] = __uint_as_float(qraw[g][k].y) * a.scale_log2;
-        qf[g][k][2] = __uint_as_float(qraw[g][k].z) * a.scale_log2;
-        qf[g][k][3] = __uint_as_float(qraw[g][k].w) * a.scale_log2;
-      }
-  }
-  const float qk_scale = BF16 ? a.scale_log2 : 1.0f;
-
-  // --- addressing --------------------------------------------------------------
-  const uint32_t row_bytes = (uint32_t)a.num_kv_heads * D * sizeof(T);
-  const int64_t block_bytes = (int64_t)row_bytes << a.log2_bs;
-  const uint32_t lane_col = (uint32_t)(kvh * D + c * VEC) * sizeof(T);
-  constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
-  const char* kp = (const char*)a.k_pool;
-  const char* vp = (const char*)a.v_pool;
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  const int bs_mask = (1 << a.log2_bs) - 1;
-  const int nb_max = a.num_blocks - 1;
-
-  float m_run[G], l_run[G], acc[G][CPL][VEC];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[g][k][e] = 0.f;
-  }
-
-  // Physical block of each load instruction of the tile starting at t0.  In
-  // UNIFORM mode these are wave-uniform scalar loads.  Rows are clamped to
-  // end-1, so a tile past the end still addresses valid (written) rows.
-  auto lookup = [&](int t0, int (&ph)[NI]) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if constexpr (UNIFORM) {
-        ph[i] = bt[min(t0 + i * TPI, end - 1) >> a.log2_bs];
-      } else {
-        ph[i] = bt[min(t0 + i * TPI + tg, end - 1) >> a.log2_bs];
-      }
-    }
-  };
+  static constexpr int VEC = S::VEC, CPL = S::CPL, LPR = S::LPR, LOG_LPR = ilog2(S::LPR);
+  static constexpr int TPI = S::TPI, NI = S::NI, TT = S::TT;
+  static constexpr bool BF16 = sizeof(T) == 2;
+  static constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
 
   struct Tile {
     uint4 k[NI][CPL];
     uint4 v[NI][CPL];
   };
+
+  const DecodeArgs& a;
+  int lane, tg, c, kvh;
+  uint32_t row_bytes, lane_col;
+  int64_t block_bytes;
+  int nb_max, bs_mask;
+  float qk_scale;
+  // current query
+  uint4 qraw[G][CPL];
+  float qf[G][CPL][4];
+  float m_run[G], l_run[G], acc[G][CPL][VEC];
+
+  __device__ WaveCtx(const DecodeArgs& args, int kv_head) : a(args), kvh(kv_head) {
+    lane = threadIdx.x & (kWave - 1);
+    tg = lane / LPR;
+    c = lane % LPR;
+    row_bytes = (uint32_t)a.num_kv_heads * D * sizeof(T);
+    block_bytes = (int64_t)row_bytes << a.log2_bs;
+    lane_col = (uint32_t)(kvh * D + c * VEC) * sizeof(T);
+    nb_max = a.num_blocks - 1;
+    bs_mask = (1 << a.log2_bs) - 1;
+    qk_scale = BF16 ? a.scale_log2 : 1.0f;
+  }
+
+  // Query token j's chunks of the G heads; scores stay unscaled and
+  // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
+  __device__ void load_query(int j) {
+    const T* qrow = (const T*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        qraw[g][k] = *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC);
+    if constexpr (!BF16) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          qf[g][k][0] = __uint_as_float(qraw[g][k].x) * a.scale_log2;
+          qf[g][k][1] = __uint_as_float(qraw[g][k].y) * a.scale_log2;
+          qf[g][k][2] = __uint_as_float(qraw[g][k].z) * a.scale_log2;
+          qf[g][k][3] = __uint_as_float(qraw[g][k].w) * a.scale_log2;
+        }
+    }
+  }
+
+  __device__ void reset() {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_run[g] = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][k][e] = 0.f;
+    }
+  }
+
+  // Physical block of each load instruction of the tile at token t0 of the
+  // sequence whose table row is bt (keys < end).  Rows are clamped to end-1,
+  // so a tile past the end still addresses a written row.
+  __device__ void lookup(const int32_t* bt, int t0, int end, int (&ph)[NI]) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if constexpr (UNIFORM) {
+        // scalar loads: a vector load here would be waited for together with
+        // the tile loads issued before it, draining the pipeline
+        ph[i] = bt[min(t0 + i * TPI, end - 1) >> a.log2_bs];
+      } else {
+        ph[i] = bt[min(t0 + i * TPI + tg, end - 1) >> a.log2_bs];
+      }
+    }
+  }
+
   // Gather the K and V rows of the tile at t0 through the block table.
-  auto issue = [&](Tile& tl, int t0, const int (&ph)[NI]) {
+  __device__ void issue(Tile& tl, int t0, int end, const int (&ph)[NI]) const {
+    const char* kp = (const char*)a.k_pool;
+    const char* vp = (const char*)a.v_pool;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int tok = min(t0 + i * TPI + tg, end - 1);  // clamp rows past the end
@@ -245,9 +210,10 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(DecodeArgs a)
 #pragma unroll
       for (int k = 0; k < CPL; ++k) tl.v[i][k] = *(const uint4*)(vb + k * kChunkStride);
     }
-  };
+  }
 
-  auto compute = [&](const Tile& tl, int t0) {
+  // Fold the tile at t0 (keys < end) into the running softmax state.
+  __device__ void compute(const Tile& tl, int t0, int end) {
     // ---- scores: partial dots over the lane's chunks, then sum the row -----
     float s[NI][G];
 #pragma unroll
@@ -336,127 +302,466 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(DecodeArgs a)
           for (int e = 0; e < VEC; ++e) acc[g][k][e] = fmaf(s[i][g], v[e], acc[g][k][e]);
       }
     }
-  };
-
-  // Software pipeline: the loads of tile t+1 are in flight while tile t is
-  // computed (two register tiles, A and B).  They are issued unconditionally
-  // -- past the end they re-read the clamped last row -- so the wait before
-  // each compute is always "all but the newest tile's loads".
-  int ph[NI];
-  lookup(start, ph);
-  Tile ta, tb;
-  issue(ta, start, ph);
-  lookup(start + TT, ph);
-  for (int t0 = start;;) {
-    issue(tb, t0 + TT, ph);
-    lookup(t0 + 2 * TT, ph);
-    compute(ta, t0);
-    t0 += TT;
-    if (t0 >= end) break;
-    issue(ta, t0 + TT, ph);
-    lookup(t0 + 2 * TT, ph);
-    compute(tb, t0);
-    t0 += TT;
-    if (t0 >= end) break;
   }
 
-  // --- combine the token groups and write ---------------------------------------
+  // Fold the keys [start, end) of the sequence with table row bt, pipelined:
+  // the loads of tile t+1 are in flight while tile t is computed (two register
+  // tiles).  Loads are issued unconditionally -- past the end they re-read the
+  // clamped last row -- so each compute waits for exactly one older tile.
+  // Requires start < end.
+  __device__ void run(const int32_t* bt, int start, int end) {
+    int ph[NI];
+    lookup(bt, start, end, ph);
+    Tile ta, tb;
+    issue(ta, start, end, ph);
+    lookup(bt, start + TT, end, ph);
+    for (int t0 = start;;) {
+      issue(tb, t0 + TT, end, ph);
+      lookup(bt, t0 + 2 * TT, end, ph);
+      compute(ta, t0, end);
+      t0 += TT;
+      if (t0 >= end) break;
+      issue(ta, t0 + TT, end, ph);
+      lookup(bt, t0 + 2 * TT, end, ph);
+      compute(tb, t0, end);
+      t0 += TT;
+      if (t0 >= end) break;
+    }
+  }
+
+  // Sum the token groups: afterwards lanes with tg == 0 hold the full acc of
+  // their chunks and every lane the full l.
+  __device__ void combine(float (&l)[G]) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = reduce_groups<LOG_LPR>(l_run[g], OpSum());
+    for (int g = 0; g < G; ++g) {
+      l[g] = reduce_groups<LOG_LPR>(l_run[g], OpSum());
 #pragma unroll
-    for (int k = 0; k < CPL; ++k)
+      for (int k = 0; k < CPL; ++k)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[g][k][e] = reduce_groups<LOG_LPR>(acc[g][k][e], OpSum());
-    const float inv = 1.f / l;
-    const int h = h0 + g;
-    if (tg == 0) {
+        for (int e = 0; e < VEC; ++e) acc[g][k][e] = reduce_groups<LOG_LPR>(acc[g][k][e], OpSum());
+    }
+  }
+
+  // Normalised output of query j (dtype T) -- after combine().
+  __device__ void store_out(void* out, int j, const float (&l)[G]) const {
+    if (tg != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float inv = 1.f / l[g];
+      T* o = (T*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D;
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         const int col = (c + k * LPR) * VEC;
-        if constexpr (SPLIT) {
-          float* po = a.part_o + (((int64_t)j * a.num_q_heads + h) * a.max_partitions + part) * D + col;
-#pragma unroll
-          for (int e = 0; e < VEC; e += 4)
-            *(float4*)(po + e) = make_float4(acc[g][k][e] * inv, acc[g][k][e + 1] * inv,
-                                             acc[g][k][e + 2] * inv, acc[g][k][e + 3] * inv);
+        if constexpr (BF16) {
+          uint4 w;
+          w.x = pack_bf16x2(acc[g][k][0] * inv, acc[g][k][1] * inv);
+          w.y = pack_bf16x2(acc[g][k][2] * inv, acc[g][k][3] * inv);
+          w.z = pack_bf16x2(acc[g][k][4] * inv, acc[g][k][5] * inv);
+          w.w = pack_bf16x2(acc[g][k][6] * inv, acc[g][k][7] * inv);
+          *(uint4*)(o + col) = w;
         } else {
-          T* o = (T*)a.out + ((int64_t)j * a.num_q_heads + h) * D + col;
-          if constexpr (BF16) {
-            uint4 w;
-            w.x = pack_bf16x2(acc[g][k][0] * inv, acc[g][k][1] * inv);
-            w.y = pack_bf16x2(acc[g][k][2] * inv, acc[g][k][3] * inv);
-            w.z = pack_bf16x2(acc[g][k][4] * inv, acc[g][k][5] * inv);
-            w.w = pack_bf16x2(acc[g][k][6] * inv, acc[g][k][7] * inv);
-            *(uint4*)o = w;
-          } else {
-            *(float4*)o = make_float4(acc[g][k][0] * inv, acc[g][k][1] * inv,
-                                      acc[g][k][2] * inv, acc[g][k][3] * inv);
-          }
+          *(float4*)(o + col) = make_float4(acc[g][k][0] * inv, acc[g][k][1] * inv,
+                                            acc[g][k][2] * inv, acc[g][k][3] * inv);
         }
       }
-      if constexpr (SPLIT) {
-        if (c == 0)
-          a.part_lse[((int64_t)j * a.num_q_heads + h) * a.max_partitions + part] =
-              (m_run[g] + __log2f(l)) * 0.69314718055994530942f;
+    }
+  }
+
+  // Partial (o, lse) of head h = kvh*G + g at o_row(h) / lse_at(h) -- after combine().
+  template <class ORow, class LseAt>
+  __device__ void store_partial(ORow o_row, LseAt lse_at, const float (&l)[G]) const {
+    if (tg != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int h = kvh * G + g;
+      const float inv = 1.f / l[g];
+      float* po = o_row(h);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const int col = (c + k * LPR) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          *(float4*)(po + col + e) = make_float4(acc[g][k][e] * inv, acc[g][k][e + 1] * inv,
+                                                 acc[g][k][e + 2] * inv, acc[g][k][e + 3] * inv);
       }
+      if (c == 0) *lse_at(h) = (m_run[g] + __log2f(l[g])) * kLn2;
+    }
+  }
+
+  __device__ void store_zero(void* out, int j) const {
+    if (tg != 0) return;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+        *(uint4*)((T*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D +
+                  (c + k * LPR) * VEC) = make_uint4(0, 0, 0, 0);
+  }
+};
+
+// Query token j -> (sequence, number of query tokens of that sequence, first
+// query token of the sequence), binary search over cu_q_lens.
+__device__ __forceinline__ void locate(const DecodeArgs& a, int j, int& b, int& q_len,
+                                       int& q_first) {
+  b = j;
+  q_first = j;
+  q_len = 1;
+  if (a.cu_q_lens != nullptr) {
+    int lo = 0, hi = a.num_seqs - 1;  // last b with cu[b] <= j
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_q_lens[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    q_first = a.cu_q_lens[b];
+    q_len = a.cu_q_lens[b + 1] - q_first;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grid kernel: blockIdx.x = query token * groups + KV-head group (groups vary
+// fastest, so the heads of one block are read at about the same time),
+// blockIdx.z = partition, dispatched last-first so that the long sequences'
+// tails start early.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int G, bool SPLIT, bool UNIFORM>
+__global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
+    DecodeArgs a, const int32_t* __restrict__ block_tables) {
+  const int groups = a.num_kv_heads / a.waves_per_group;
+  const int j = blockIdx.x / groups;
+  const int kvh = (blockIdx.x % groups) * a.waves_per_group + threadIdx.x / kWave;
+  const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
+
+  int b, q_len, q_first;
+  locate(a, j, b, q_len, q_first);
+  const int cap = a.max_blocks << a.log2_bs;
+  const int len = min(max(a.seq_lens[b], 0), cap);
+  const int key_end = len - q_len + (j - q_first) + 1;  // keys 0 .. position
+  int start = 0, end = key_end;
+  if constexpr (SPLIT) {
+    if (q_len > 1) {
+      if (part != 0) return;  // multi-query sequences: one partition
+    } else {
+      start = part * a.partition_size;
+      end = min(key_end, start + a.partition_size);
+    }
+    if (start >= end) return;  // this partition holds no key
+  }
+  WaveCtx<T, D, G, UNIFORM> w(a, kvh);
+  if constexpr (!SPLIT) {
+    if (end <= 0) {
+      w.store_zero(a.out, j);
+      return;
+    }
+  }
+  w.load_query(j);
+  w.reset();
+  w.run(block_tables + (int64_t)b * a.max_blocks, start, end);
+  float l[G];
+  w.combine(l);
+  if constexpr (SPLIT) {
+    const int64_t base = (int64_t)j * a.num_q_heads;
+    w.store_partial(
+        [&](int h) { return a.part_o + ((base + h) * a.max_partitions + part) * D; },
+        [&](int h) { return a.part_lse + (base + h) * a.max_partitions + part; }, l);
+  } else {
+    w.store_out(a.out, j, l);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Balanced streaming decode (one query token per sequence).
+//
+// All (sequence, tile) pairs are laid end to end -- sequence b contributes
+// tiles(b) = ceil(len_b / TT) -- and cut into R equal slices, one per
+// workgroup slot that is resident on the device at once; the KV-head groups
+// of a slice are consecutive workgroups.  A workgroup computes the prefix sums
+// cum[] of tiles(b) in LDS, walks its slice, writes the output of every
+// sequence that lies wholly inside the slice, and stores (o, lse) for a
+// sequence that the slice cuts: slot 0 if it is the slice's first sequence,
+// slot 1 if it is its last.  stream_fixup_kernel merges the cut sequences.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t slice_start(int64_t r, int64_t T, int64_t R) {
+  return r * T / R;
+}
+
+// An LDS value every lane reads at the same address, moved to a scalar register.
+__device__ __forceinline__ int uniform_lds(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
+
+// block_tables is a separate __restrict__ argument: nothing the kernel stores
+// can alias it, so its wave-uniform lookups stay scalar loads after stores.
+template <typename T, int D, int G, bool UNIFORM>
+__global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
+    DecodeArgs a, StreamArgs s, const int32_t* __restrict__ block_tables) {
+  using W = WaveCtx<T, D, G, UNIFORM>;
+  constexpr int TT = W::TT;
+  extern __shared__ int lds[];
+  const int B = a.num_seqs;
+  int* cum = lds;            // [B + 1]
+  int* ends = lds + B + 1;   // [B]
+  const int groups = a.num_kv_heads / a.waves_per_group;
+  const int r = blockIdx.x / groups;
+  const int kvh = (blockIdx.x % groups) * a.waves_per_group + threadIdx.x / kWave;
+  const int cap = a.max_blocks << a.log2_bs;
+
+  // ---- prefix sums of tiles per sequence -------------------------------------
+  // every thread loads lengths (one memory round trip), wave 0 scans in LDS
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const int len = min(max(a.seq_lens[i], 0), cap);
+    ends[i] = len;
+    cum[i + 1] = (len + TT - 1) / TT;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int carry = 0;
+    if (lane == 0) cum[0] = 0;
+    for (int base = 0; base < B; base += kWave) {
+      const int i = base + lane;
+      int x = i < B ? cum[i + 1] : 0;  // inclusive scan across the wave
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+      }
+      if (i < B) cum[i + 1] = carry + x;
+      carry += __shfl(x, kWave - 1, kWave);
+    }
+  }
+  __syncthreads();
+  const int64_t total = uniform_lds(&cum[B]);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= B; i += blockDim.x) s.cum[i] = cum[i];
+  }
+  const int64_t t_begin = slice_start(r, total, s.num_slices);
+  const int64_t t_end = slice_start(r + 1, total, s.num_slices);
+  if (t_begin >= t_end) return;
+
+  // first sequence of the slice: the last b with cum[b] <= t_begin
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform_lds(&cum[mid]) <= t_begin) lo = mid; else hi = mid - 1;
+  }
+  const int b_first = lo;
+
+  W w(a, kvh);
+  for (int b = b_first; b < B; ++b) {
+    const int c_lo = uniform_lds(&cum[b]);
+    const int c_hi = uniform_lds(&cum[b + 1]);
+    const int64_t seg_lo = max(t_begin, (int64_t)c_lo);
+    const int64_t seg_hi = min(t_end, (int64_t)c_hi);
+    if (seg_lo < seg_hi) {
+      const int start = (int)(seg_lo - c_lo) * TT;
+      const int stop = min(uniform_lds(&ends[b]), (int)(seg_hi - c_lo) * TT);
+      w.load_query(b);
+      w.reset();
+      w.run(block_tables + (int64_t)b * a.max_blocks, start, stop);
+      float l[G];
+      w.combine(l);
+      if (seg_lo == c_lo && seg_hi == c_hi) {
+        w.store_out(a.out, b, l);
+      } else {
+        const int slot = (b == b_first) ? 0 : 1;
+        const int64_t base = ((int64_t)r * 2 + slot) * a.num_q_heads;
+        w.store_partial([&](int h) { return s.part_o + (base + h) * D; },
+                        [&](int h) { return s.part_lse + base + h; }, l);
+      }
+    }
+    if (c_hi >= t_end) break;
+  }
+}
+
+// Merge the partials of every sequence cut by slice boundaries; zero rows for
+// sequences without keys.  One wave per (sequence, head), kFixupWaves heads
+// per workgroup; lane s handles the s-th slice of the sequence (64 at a time).
+constexpr int kFixupWaves = 4;
+
+__global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(DecodeArgs a,
+                                                                          StreamArgs s) {
+  const int b = blockIdx.x;
+  const int h = blockIdx.y * kFixupWaves + threadIdx.x / kWave;
+  if (h >= a.num_q_heads) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int D = a.head_dim;
+  const int64_t T = s.cum[a.num_seqs];
+  const int64_t c0 = s.cum[b], c1 = s.cum[b + 1];
+  const int64_t R = s.num_slices;
+  const bool bf16 = a.dtype == PA_BF16;
+  const int64_t row = (int64_t)b * a.num_q_heads + h;
+  if (c0 == c1) {  // no key: zero row
+    for (int d = lane; d < D; d += kWave) {
+      if (bf16) ((uint16_t*)a.out)[row * D + d] = 0;
+      else ((float*)a.out)[row * D + d] = 0.f;
+    }
+    return;
+  }
+  // slice holding tile t: the largest r with slice_start(r) <= t
+  const int64_t r1 = ((c0 + 1) * R - 1) / T;
+  const int64_t r2 = (c1 * R - 1) / T;
+  if (r1 == r2) return;  // wholly inside one slice: already written
+  const int nseg = (int)(r2 - r1 + 1);
+  // partial index of slice r1 + k, or -1 for an empty slice
+  auto seg_index = [&](int k) -> int64_t {
+    const int64_t r = r1 + k;
+    if (slice_start(r, T, R) == slice_start(r + 1, T, R)) return -1;
+    const int slot = (k == 0 && slice_start(r1, T, R) < c0) ? 1 : 0;
+    return (r * 2 + slot) * a.num_q_heads + h;
+  };
+  float m = -INFINITY;
+  for (int k = lane; k < nseg; k += kWave) {
+    const int64_t idx = seg_index(k);
+    if (idx >= 0) m = fmaxf(m, s.part_lse[idx]);
+  }
+  m = reduce_levels<0, 6>(m, OpMax());
+  float den = 0.f;
+  float o[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane + 64 * i
+  for (int k0 = 0; k0 < nseg; k0 += kWave) {
+    const int k = k0 + lane;
+    const int64_t idx = k < nseg ? seg_index(k) : -1;
+    const float wgt = idx >= 0 ? __expf(s.part_lse[idx] - m) : 0.f;
+    den += wgt;
+    const int n = min(kWave, nseg - k0);
+    for (int q = 0; q < n; ++q) {  // slices of this chunk, weights from lane q
+      const float wq = __shfl(wgt, q, kWave);
+      const int64_t iq = __shfl((long long)idx, q, kWave);
+      if (iq < 0) continue;
+      const float* po = s.part_o + iq * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + i * kWave < D) o[i] = fmaf(wq, po[lane + i * kWave], o[i]);
+    }
+  }
+  den = reduce_levels<0, 6>(den, OpSum());
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = lane + i * kWave;
+    if (d < D) {
+      if (bf16) ((__bf16*)a.out)[row * D + d] = (__bf16)(o[i] * inv);
+      else ((float*)a.out)[row * D + d] = o[i] * inv;
     }
   }
 }
 
 template <typename T, int D, int G>
-pa_status launch_typed(const DecodeArgs& a, bool split, hipStream_t stream) {
+constexpr int tpi() {
+  return Shape<T, D, G>::TPI;
+}
+
+template <typename T, int D, int G>
+pa_status launch_grid(const DecodeArgs& a, bool split, hipStream_t stream) {
   const int groups = a.num_kv_heads / a.waves_per_group;
-#if PA_GROUP_MAJOR
-  const dim3 grid(groups, a.num_q_tokens, split ? a.max_partitions : 1);
-#else
-  const dim3 grid(a.num_q_tokens, groups, split ? a.max_partitions : 1);
-#endif
+  const dim3 grid((uint32_t)((int64_t)a.num_q_tokens * groups), 1, split ? a.max_partitions : 1);
   const dim3 block(a.waves_per_group * kWave);
-  const bool uniform = (1 << a.log2_bs) >= Shape<T, D, G>::TPI;
+  const bool uniform = (1 << a.log2_bs) >= tpi<T, D, G>();
   if (split) {
     if (uniform)
-      hipLaunchKernelGGL((decode_kernel<T, D, G, true, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<T, D, G, true, true>), grid, block, 0, stream, a,
+                         a.block_tables);
     else
-      hipLaunchKernelGGL((decode_kernel<T, D, G, true, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<T, D, G, true, false>), grid, block, 0, stream, a,
+                         a.block_tables);
   } else {
     if (uniform)
-      hipLaunchKernelGGL((decode_kernel<T, D, G, false, true>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<T, D, G, false, true>), grid, block, 0, stream, a,
+                         a.block_tables);
     else
-      hipLaunchKernelGGL((decode_kernel<T, D, G, false, false>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((decode_kernel<T, D, G, false, false>), grid, block, 0, stream, a,
+                         a.block_tables);
   }
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-template <typename T, int D>
-pa_status dispatch_g(const DecodeArgs& a, bool split, hipStream_t s) {
-  switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_typed<T, D, 1>(a, split, s);
-    case 2: return launch_typed<T, D, 2>(a, split, s);
-    case 4: return launch_typed<T, D, 4>(a, split, s);
-    case 8: return launch_typed<T, D, 8>(a, split, s);
-    default: return PA_ERR_UNSUPPORTED;
-  }
+template <typename T, int D, int G>
+pa_status stream_per_cu(const DecodeArgs& a, int* per_cu) {
+  const size_t lds = stream_lds_bytes(a.num_seqs);
+  const int threads = a.waves_per_group * kWave;
+  hipError_t e;
+  if ((1 << a.log2_bs) >= tpi<T, D, G>())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        per_cu, decode_stream_kernel<T, D, G, true>, threads, lds);
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        per_cu, decode_stream_kernel<T, D, G, false>, threads, lds);
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-template <typename T>
-pa_status dispatch_d(const DecodeArgs& a, bool split, hipStream_t s) {
-  switch (a.head_dim) {
-    case 32: return dispatch_g<T, 32>(a, split, s);
-    case 64: return dispatch_g<T, 64>(a, split, s);
-    case 128: return dispatch_g<T, 128>(a, split, s);
-    case 256: return dispatch_g<T, 256>(a, split, s);
-    default: return PA_ERR_UNSUPPORTED;
-  }
+template <typename T, int D, int G>
+pa_status launch_stream(const DecodeArgs& a, const StreamArgs& s, hipStream_t stream) {
+  const int groups = a.num_kv_heads / a.waves_per_group;
+  const dim3 grid((uint32_t)((int64_t)s.num_slices * groups));
+  const dim3 block(a.waves_per_group * kWave);
+  const size_t lds = stream_lds_bytes(a.num_seqs);
+  if ((1 << a.log2_bs) >= tpi<T, D, G>())
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, G, true>), grid, block, lds, stream, a, s,
+                       a.block_tables);
+  else
+    hipLaunchKernelGGL((decode_stream_kernel<T, D, G, false>), grid, block, lds, stream, a, s,
+                       a.block_tables);
+  if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  const dim3 fgrid(a.num_seqs, (a.num_q_heads + kFixupWaves - 1) / kFixupWaves);
+  hipLaunchKernelGGL(stream_fixup_kernel, fgrid, dim3(kFixupWaves * kWave), 0, stream, a, s);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+// (dtype, head_dim, G) -> template instance: f.template operator()<T, D, G>().
+template <class F>
+pa_status dispatch(const DecodeArgs& a, F&& f) {
+  const int g = a.num_q_heads / a.num_kv_heads;
+  auto by_g = [&](auto t, auto d) -> pa_status {
+    using T = decltype(t);
+    constexpr int Dv = decltype(d)::value;
+    switch (g) {
+      case 1: return f.template operator()<T, Dv, 1>();
+      case 2: return f.template operator()<T, Dv, 2>();
+      case 4: return f.template operator()<T, Dv, 4>();
+      case 8: return f.template operator()<T, Dv, 8>();
+      default: return PA_ERR_UNSUPPORTED;
+    }
+  };
+  auto by_d = [&](auto t) -> pa_status {
+    switch (a.head_dim) {
+      case 32: return by_g(t, std::integral_constant<int, 32>());
+      case 64: return by_g(t, std::integral_constant<int, 64>());
+      case 128: return by_g(t, std::integral_constant<int, 128>());
+      case 256: return by_g(t, std::integral_constant<int, 256>());
+      default: return PA_ERR_UNSUPPORTED;
+    }
+  };
+  if (a.dtype == PA_BF16) return by_d(uint16_t());
+  if (a.dtype == PA_F32) return by_d(float());
+  return PA_ERR_UNSUPPORTED;
 }
 
 }  // namespace
 
+size_t stream_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
+
 pa_status launch_decode(const DecodeArgs& a, bool split, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  if (a.dtype == PA_BF16) return dispatch_d<uint16_t>(a, split, s);
-  if (a.dtype == PA_F32) return dispatch_d<float>(a, split, s);
-  return PA_ERR_UNSUPPORTED;
+  return dispatch(a, [&]<typename T, int D, int G>() { return launch_grid<T, D, G>(a, split, s); });
+}
+
+pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return PA_ERR_HIP;
+  const pa_status st =
+      dispatch(a, [&]<typename T, int D, int G>() { return stream_per_cu<T, D, G>(a, &per_cu); });
+  if (st != PA_OK) return st;
+  if (per_cu < 1) return PA_ERR_UNSUPPORTED;
+  // slices = workgroups resident at once, shared out among the KV-head groups
+  const int groups = a.num_kv_heads / a.waves_per_group;
+  const int64_t n = (int64_t)per_cu * cus / groups;
+  *num_slices = (int32_t)(n < 1 ? 1 : n);
+  return PA_OK;
+}
+
+pa_status launch_decode_stream(const DecodeArgs& a, const StreamArgs& sa, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  return dispatch(a, [&]<typename T, int D, int G>() { return launch_stream<T, D, G>(a, sa, s); });
 }
 
 }  // namespace pa

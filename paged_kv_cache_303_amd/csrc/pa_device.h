@@ -117,6 +117,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// A pointer every lane holds the same value of, made provably wave-uniform
+// (scalar registers), so that loads through it with uniform indices become
+// scalar loads, counted apart from the vector loads in flight.
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(((uint64_t)hi << 32) | lo);
+}
+
 // 2^x on the transcendental unit; exact 0 for x = -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -50,8 +50,25 @@ struct ReduceArgs {
   int32_t head_dim;
 };
 
+// Workspace of the balanced streaming decode (inside the caller's workspace).
+struct StreamArgs {
+  float* part_o;       // [num_slices, 2, num_q_heads, head_dim]
+  float* part_lse;     // [num_slices, 2, num_q_heads]
+  int32_t* cum;        // [num_seqs + 1] prefix sums of tiles per sequence
+  int32_t num_slices;  // equal slices of the batch's (sequence, tile) work
+};
+
+// Sequences the streaming decode handles per launch (its LDS holds two ints
+// per sequence); larger batches use the grid kernel.
+constexpr int32_t kStreamMaxSeqs = 4096;
+size_t stream_lds_bytes(int32_t num_seqs);
+
 // Returns PA_OK, PA_ERR_UNSUPPORTED (no instance for the shape) or PA_ERR_HIP.
 pa_status launch_decode(const DecodeArgs& a, bool split, void* stream);
+// Number of slices = workgroups of the streaming kernel resident on the
+// current device at once / KV-head groups.
+pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices);
+pa_status launch_decode_stream(const DecodeArgs& a, const StreamArgs& s, void* stream);
 pa_status launch_reduce(const ReduceArgs& a, void* stream);
 pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
                           const void* v_new, const int32_t* slots, int32_t num_tokens,

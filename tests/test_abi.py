@@ -59,7 +59,7 @@ def test_layout_validation(built_library, field, value, status):
     setattr(lay, field, value)
     dummy = ctypes.c_void_p(16)
     st = lib.pa_decode(ctypes.byref(lay), dummy, dummy, dummy, dummy, dummy, 4, dummy, 1, 32,
-                       0.1, None)
+                       0.1, None, 0, None)
     assert st == status, _err(lib)
     assert "pa_decode" in _err(lib)
 
@@ -71,17 +71,17 @@ def test_decode_argument_validation(built_library):
     d = ctypes.c_void_p(16)
     nul = ctypes.c_void_p(0)
     # query heads not a multiple of KV heads; unsupported ratio; NULL pointers
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 12, 0.1, None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 8 * 16, 0.1, None) == 2
-    assert lib.pa_decode(ctypes.byref(lay), d, nul, d, d, d, 4, d, 1, 32, 0.1, None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), nul, d, d, d, d, 4, d, 1, 32, 0.1, None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 0, d, 1, 32, 0.1, None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, float("nan"), None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, -0.5, None) == 1
-    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, 0.0, None) == 1
-    assert lib.pa_decode(None, d, d, d, d, d, 4, d, 1, 32, 0.1, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 12, 0.1, None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 8 * 16, 0.1, None, 0, None) == 2
+    assert lib.pa_decode(ctypes.byref(lay), d, nul, d, d, d, 4, d, 1, 32, 0.1, None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), nul, d, d, d, d, 4, d, 1, 32, 0.1, None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 0, d, 1, 32, 0.1, None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, float("nan"), None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, -0.5, None, 0, None) == 1
+    assert lib.pa_decode(ctypes.byref(lay), d, d, d, d, d, 4, d, 1, 32, 0.0, None, 0, None) == 1
+    assert lib.pa_decode(None, d, d, d, d, d, 4, d, 1, 32, 0.1, None, 0, None) == 1
     # zero sequences is a no-op
-    assert lib.pa_decode(ctypes.byref(lay), nul, nul, d, d, nul, 4, nul, 0, 32, 0.1, None) == 0
+    assert lib.pa_decode(ctypes.byref(lay), nul, nul, d, d, nul, 4, nul, 0, 32, 0.1, None, 0, None) == 0
 
 
 def test_split_argument_validation(built_library):

@@ -66,9 +66,14 @@ def _check_all_paths(pa, w, st_p, st_o, tokens=None, partitions=(None,)):
         stats[f"split{p or w.partition_size}"] = check_attention(out, ref, w.dtype, rows,
                                                                  f"{w.name} split P={p}")
     if w.cu_q_lens is None:
-        out = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
-                             st_p["seq_lens"], w.scale)
+        args = (st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
+                st_p["seq_lens"], w.scale)
+        out = binding.decode(*args)
         stats["single_pass"] = check_attention(out, ref, w.dtype, rows, f"{w.name} single pass")
+        ws = binding.decode_workspace(st_p["k_pool"], len(w.seq_lens), w.num_q_heads)
+        if ws is not None:
+            out = binding.decode(*args, workspace=ws)
+            stats["balanced"] = check_attention(out, ref, w.dtype, rows, f"{w.name} balanced")
     print(f"[parity] {w.name} {w.dtype}: " +
           ", ".join(f"{k} max_err={v[0]:.2e} rel={v[1]:.2e}" for k, v in stats.items()),
           flush=True)
@@ -188,6 +193,51 @@ def test_split_partials_match_oracle(pa, dtype):
         np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=tol)
 
 
+@pytest.mark.parametrize("lens", [
+    [3000, 1, 2],                      # one sequence spans many slices
+    [1] * 300,                         # fewer tiles than slices
+    [7],                               # a single short sequence
+    [8192] + [16] * 40 + [4000, 33],   # long sequences cut everywhere
+    list(range(1, 600, 7)),            # ragged, every tail length
+], ids=["long_short", "all_one", "single", "mixed", "ragged"])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_balanced_slicing(pa, lens, dtype):
+    binding, runner, _ = pa
+    w = wl.custom_decode(21, lens, num_blocks=2048, block_size=16, num_q_heads=16,
+                         num_kv_heads=4, head_dim=128, dtype=dtype, name="slicing")
+    st_p, st_o = _both(pa, w)
+    ref = orun.attention(w, st_o)
+    ws = binding.decode_workspace(st_p["k_pool"], len(lens), w.num_q_heads)
+    assert ws is not None
+    out = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
+                         st_p["seq_lens"], w.scale, workspace=ws)
+    check_attention(out, ref, dtype, what="balanced slicing")
+    # zero-length sequences: zero rows, the others unchanged
+    sl = st_p["seq_lens"].clone()
+    zero = list(range(0, len(lens), 3))
+    sl[zero] = 0
+    out = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"], sl,
+                         w.scale, workspace=ws)
+    o = to_f64(out)
+    assert (o[zero] == 0).all()
+    keep = [i for i in range(len(lens)) if i not in zero]
+    if keep:
+        check_attention(out, ref, dtype, rows=keep, what="balanced with empty rows")
+
+
+def test_balanced_falls_back_for_huge_batches(pa):
+    binding, _, dev = pa
+    k = torch.zeros((8, 16, 2, 128), dtype=torch.bfloat16, device=dev)
+    assert binding.decode_workspace_size(k, 5000, 8) == 0
+    assert binding.decode_workspace_size(k, 4096, 8) > 0
+    with pytest.raises(binding.PagedAttentionError):
+        q = torch.zeros((4, 8, 128), dtype=torch.bfloat16, device=dev)
+        bt = torch.zeros((4, 1), dtype=torch.int32, device=dev)
+        sl = torch.ones(4, dtype=torch.int32, device=dev)
+        tiny = torch.empty(16, dtype=torch.uint8, device=dev)
+        binding.decode(q, k, k, bt, sl, 0.1, workspace=tiny)  # too small: rejected on host
+
+
 def test_zero_length_and_empty_batch(pa):
     binding, _, dev = pa
     k = torch.full((8, 16, 2, 128), float("nan"), dtype=torch.bfloat16, device=dev)
@@ -252,6 +302,12 @@ def test_deterministic(pa):
                        st_p["seq_lens"], w.scale)
     d = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
                        st_p["seq_lens"], w.scale)
+    ws = binding.decode_workspace(st_p["k_pool"], len(w.seq_lens), w.num_q_heads)
+    e = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
+                       st_p["seq_lens"], w.scale, workspace=ws)
+    f = binding.decode(st_p["q"], st_p["k_pool"], st_p["v_pool"], st_p["block_tables"],
+                       st_p["seq_lens"], w.scale, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(c.view(torch.int16), d.view(torch.int16))
+    assert torch.equal(e.view(torch.int16), f.view(torch.int16))
