@@ -113,18 +113,22 @@ struct WaveCtx {
     uint4 v[NI][CPL];
   };
 
+  // The current query lives in LDS, not registers: [G][CPL][LPR] 16-byte
+  // chunks per wave (fp32: pre-scaled), read back once per tile; the lanes
+  // of one chunk column read the same address (broadcast).
+  static constexpr int kQChunks = G * CPL * LPR;
+
   const DecodeArgs& a;
+  uint4* qs;  // this wave's kQChunks chunks in LDS
   int lane, tg, c, kvh;
   uint32_t row_bytes, lane_col;
   int64_t block_bytes;
   int nb_max, bs_mask;
   float qk_scale;
-  // current query
-  uint4 qraw[G][CPL];
-  float qf[G][CPL][4];
   float m_run[G], l_run[G], acc[G][CPL][VEC];
 
-  __device__ WaveCtx(const DecodeArgs& args, int kv_head) : a(args), kvh(kv_head) {
+  __device__ WaveCtx(const DecodeArgs& args, int kv_head, uint4* q_lds)
+      : a(args), qs(q_lds), kvh(kv_head) {
     lane = threadIdx.x & (kWave - 1);
     tg = lane / LPR;
     c = lane % LPR;
@@ -136,26 +140,30 @@ struct WaveCtx {
     qk_scale = BF16 ? a.scale_log2 : 1.0f;
   }
 
-  // Query token j's chunks of the G heads; scores stay unscaled and
+  // Query token j's chunks of the G heads into LDS; scores stay unscaled and
   // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
   __device__ void load_query(int j) {
     const T* qrow = (const T*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-        qraw[g][k] = *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC);
-    if constexpr (!BF16) {
+    if (tg == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
-          qf[g][k][0] = __uint_as_float(qraw[g][k].x) * a.scale_log2;
-          qf[g][k][1] = __uint_as_float(qraw[g][k].y) * a.scale_log2;
-          qf[g][k][2] = __uint_as_float(qraw[g][k].z) * a.scale_log2;
-          qf[g][k][3] = __uint_as_float(qraw[g][k].w) * a.scale_log2;
+          uint4 v = *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC);
+          if constexpr (!BF16) {
+            v.x = __float_as_uint(__uint_as_float(v.x) * a.scale_log2);
+            v.y = __float_as_uint(__uint_as_float(v.y) * a.scale_log2);
+            v.z = __float_as_uint(__uint_as_float(v.z) * a.scale_log2);
+            v.w = __float_as_uint(__uint_as_float(v.w) * a.scale_log2);
+          }
+          qs[(g * CPL + k) * LPR + c] = v;
         }
     }
+    // the wave's own LDS writes must land before its reads (no other wave
+    // touches this region)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   __device__ void reset() {
@@ -187,28 +195,47 @@ struct WaveCtx {
   }
 
   // Gather the K and V rows of the tile at t0 through the block table.
+  //
+  // UNIFORM: instruction i reads rows t0 + i*TPI .. +TPI-1 of the block that
+  // holds its first row (clamped to the range's last block), so the block
+  // base is wave-uniform (scalar registers) and every lane adds the same
+  // loop-invariant offset (tg rows down, its chunk across): no per-tile
+  // vector address arithmetic.  Rows at or past `end` stay inside that
+  // allocated block -- memory-safe -- and compute() masks them (their bytes
+  // may be unwritten NaN poison).  Otherwise each lane looks up its own row,
+  // clamped to end-1.
   __device__ void issue(Tile& tl, int t0, int end, const int (&ph)[NI]) const {
     const char* kp = (const char*)a.k_pool;
     const char* vp = (const char*)a.v_pool;
+    if constexpr (UNIFORM) {
+      // buffer loads: descriptor of the block (scalar), row offset (scalar),
+      // lane offset (one loop-invariant vector register)
+      const uint32_t lane_off = (uint32_t)tg * row_bytes + lane_col;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int tok = min(t0 + i * TPI + tg, end - 1);  // clamp rows past the end
-      const int phys = min(max(ph[i], 0), nb_max);
-      uint32_t off;
-      if constexpr (UNIFORM) {
-        // the TPI rows of this instruction lie in one block: the block of its
-        // first (clamped) row.
-        const int blk0 = min(t0 + i * TPI, end - 1) >> a.log2_bs;
-        off = (uint32_t)(tok - (blk0 << a.log2_bs)) * row_bytes + lane_col;
-      } else {
-        off = (uint32_t)(tok & bs_mask) * row_bytes + lane_col;
+      for (int i = 0; i < NI; ++i) {
+        const int phys = min(max(ph[i], 0), nb_max);
+        const int64_t blk = phys * block_bytes;
+        const uint32_t row = (uint32_t)((t0 + i * TPI) & bs_mask) * row_bytes;
+        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kp + blk, (uint32_t)block_bytes);
+        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vp + blk, (uint32_t)block_bytes);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) tl.k[i][k] = buffer_load16(kr, lane_off + k * kChunkStride, row);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16(vr, lane_off + k * kChunkStride, row);
       }
-      const char* kb = kp + phys * block_bytes + off;
-      const char* vb = vp + phys * block_bytes + off;
+    } else {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) tl.k[i][k] = *(const uint4*)(kb + k * kChunkStride);
+      for (int i = 0; i < NI; ++i) {
+        const int tok = min(t0 + i * TPI + tg, end - 1);  // clamp rows past the end
+        const int phys = min(max(ph[i], 0), nb_max);
+        const uint32_t off = (uint32_t)(tok & bs_mask) * row_bytes + lane_col;
+        const char* kb = kp + phys * block_bytes + off;
+        const char* vb = vp + phys * block_bytes + off;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) tl.v[i][k] = *(const uint4*)(vb + k * kChunkStride);
+        for (int k = 0; k < CPL; ++k) tl.k[i][k] = *(const uint4*)(kb + k * kChunkStride);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) tl.v[i][k] = *(const uint4*)(vb + k * kChunkStride);
+      }
     }
   }
 
@@ -217,28 +244,38 @@ struct WaveCtx {
     // ---- scores: partial dots over the lane's chunks, then sum the row -----
     float s[NI][G];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
+      for (int g = 0; g < G; ++g) s[i][g] = 0.f;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        const uint4 qv = qs[(g * CPL + k) * LPR + c];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float d = s[i][g];
           if constexpr (BF16) {
-            d = dot2_bf16(qraw[g][k].x, tl.k[i][k].x, d);
-            d = dot2_bf16(qraw[g][k].y, tl.k[i][k].y, d);
-            d = dot2_bf16(qraw[g][k].z, tl.k[i][k].z, d);
-            d = dot2_bf16(qraw[g][k].w, tl.k[i][k].w, d);
+            d = dot2_bf16(qv.x, tl.k[i][k].x, d);
+            d = dot2_bf16(qv.y, tl.k[i][k].y, d);
+            d = dot2_bf16(qv.z, tl.k[i][k].z, d);
+            d = dot2_bf16(qv.w, tl.k[i][k].w, d);
           } else {
-            d = fmaf(qf[g][k][0], __uint_as_float(tl.k[i][k].x), d);
-            d = fmaf(qf[g][k][1], __uint_as_float(tl.k[i][k].y), d);
-            d = fmaf(qf[g][k][2], __uint_as_float(tl.k[i][k].z), d);
-            d = fmaf(qf[g][k][3], __uint_as_float(tl.k[i][k].w), d);
+            d = fmaf(__uint_as_float(qv.x), __uint_as_float(tl.k[i][k].x), d);
+            d = fmaf(__uint_as_float(qv.y), __uint_as_float(tl.k[i][k].y), d);
+            d = fmaf(__uint_as_float(qv.z), __uint_as_float(tl.k[i][k].z), d);
+            d = fmaf(__uint_as_float(qv.w), __uint_as_float(tl.k[i][k].w), d);
           }
+          s[i][g] = d;
         }
-        s[i][g] = reduce_levels<0, LOG_LPR>(d, OpSum());
       }
     }
-    if (t0 + TT > end) {  // tail tile: rows past the end get probability 0
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[i][g] = reduce_levels<0, LOG_LPR>(s[i][g], OpSum());
+    const bool tail = t0 + TT > end;
+    if (tail) {  // rows past the end get probability 0
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const bool valid = (t0 + i * TPI + tg) < end;
@@ -295,6 +332,11 @@ struct WaveCtx {
         } else {
           v[0] = __uint_as_float(tl.v[i][k].x); v[1] = __uint_as_float(tl.v[i][k].y);
           v[2] = __uint_as_float(tl.v[i][k].z); v[3] = __uint_as_float(tl.v[i][k].w);
+        }
+        if (UNIFORM && tail) {  // masked rows may hold NaN poison: select, never multiply
+          const bool valid = (t0 + i * TPI + tg) < end;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[e] = valid ? v[e] : 0.f;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g)
@@ -447,7 +489,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
     }
     if (start >= end) return;  // this partition holds no key
   }
-  WaveCtx<T, D, G, UNIFORM> w(a, kvh);
+  using W = WaveCtx<T, D, G, UNIFORM>;
+  __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
+  W w(a, kvh, q_lds[threadIdx.x / kWave]);
   if constexpr (!SPLIT) {
     if (end <= 0) {
       w.store_zero(a.out, j);
@@ -545,7 +589,8 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   }
   const int b_first = lo;
 
-  W w(a, kvh);
+  __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
+  W w(a, kvh, q_lds[threadIdx.x / kWave]);
   for (int b = b_first; b < B; ++b) {
     const int c_lo = uniform_lds(&cum[b]);
     const int c_hi = uniform_lds(&cum[b + 1]);

@@ -128,6 +128,21 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
   return (T*)(((uint64_t)hi << 32) | lo);
 }
 
+// Buffer resource for `bytes` bytes at `base` (raw, untyped 32-bit data
+// format); loads through it are bounds-checked against `bytes` (reads past
+// the end return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// 16-byte load at voff (per lane) + soff (wave-uniform) within a buffer.
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                               uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // 2^x on the transcendental unit; exact 0 for x = -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
