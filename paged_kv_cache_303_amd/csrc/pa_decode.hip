@@ -55,7 +55,7 @@ struct Elt<uint16_t> {  // bfloat16 bit patterns
 };
 
 #ifndef PA_TILE_TOKENS
-#define PA_TILE_TOKENS 32  // target tokens per tile (per wave, per KV head)
+#define PA_TILE_TOKENS 16  // target tokens per tile (per wave, per KV head)
 #endif
 #ifndef PA_MAX_TILE_LOADS
 #define PA_MAX_TILE_LOADS 8  // 16-byte loads per lane per tile (K or V), hot shapes
