@@ -43,6 +43,14 @@ namespace {
 
 constexpr int kMaxWaves = 8;  // workgroup = up to 8 KV heads
 
+// Index of the wave in its workgroup, as a scalar: the compiler cannot tell
+// that threadIdx.x / 64 is the same on every lane of a wave, and values
+// derived from it would otherwise live in vector registers and turn the
+// branches on them into exec-masked code.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+}
+
 template <typename T>
 struct Elt;
 template <>
@@ -295,7 +303,7 @@ struct WaveCtx {
       mt[g] = reduce_groups<LOG_LPR>(mx, OpMax()) * qk_scale;
       move |= mt[g] > m_run[g] + kLazy;
     }
-    if (move) {  // same outcome on every lane of the wave
+    if (__builtin_amdgcn_readfirstlane((int)move)) {  // same on every lane: make it scalar
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float m_new = fmaxf(m_run[g], mt[g]);
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
     DecodeArgs a, const int32_t* __restrict__ block_tables) {
   const int groups = a.num_kv_heads / a.waves_per_group;
   const int j = blockIdx.x / groups;
-  const int kvh = (blockIdx.x % groups) * a.waves_per_group + threadIdx.x / kWave;
+  const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
   const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
 
   int b, q_len, q_first;
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
   }
   using W = WaveCtx<T, D, G, UNIFORM>;
   __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
-  W w(a, kvh, q_lds[threadIdx.x / kWave]);
+  W w(a, kvh, q_lds[wave_id()]);
   if constexpr (!SPLIT) {
     if (end <= 0) {
       w.store_zero(a.out, j);
@@ -545,7 +553,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   int* ends = lds + B + 1;   // [B]
   const int groups = a.num_kv_heads / a.waves_per_group;
   const int r = blockIdx.x / groups;
-  const int kvh = (blockIdx.x % groups) * a.waves_per_group + threadIdx.x / kWave;
+  const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
   const int cap = a.max_blocks << a.log2_bs;
 
   // ---- prefix sums of tiles per sequence -------------------------------------
@@ -590,7 +598,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   const int b_first = lo;
 
   __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
-  W w(a, kvh, q_lds[threadIdx.x / kWave]);
+  W w(a, kvh, q_lds[wave_id()]);
   for (int b = b_first; b < B; ++b) {
     const int c_lo = uniform_lds(&cum[b]);
     const int c_hi = uniform_lds(&cum[b + 1]);
@@ -625,7 +633,7 @@ constexpr int kFixupWaves = 4;
 __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(DecodeArgs a,
                                                                           StreamArgs s) {
   const int b = blockIdx.x;
-  const int h = blockIdx.y * kFixupWaves + threadIdx.x / kWave;
+  const int h = blockIdx.y * kFixupWaves + wave_id();
   if (h >= a.num_q_heads) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int D = a.head_dim;
