@@ -147,9 +147,11 @@ pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
  *                  (chunked prefill, "LLM 推理引擎的内存管理与调度" §8).
  *   part_o       : fp32 [num_q_tokens, num_q_heads, max_partitions, head_dim]
  *   part_lse     : fp32 [num_q_tokens, num_q_heads, max_partitions]
- * A query of a single-query sequence has ceil(key_end/partition_size)
- * partitions; every query of a multi-query sequence has exactly one
- * partition covering all the keys it sees.  Only those entries are written.
+ * Every query has ceil(key_end/partition_size) partitions, key_end = its
+ * position + 1; only those entries are written.  The queries of multi-query
+ * sequences (prefill chunks) run on the matrix cores for bf16 pools (tiles of
+ * 64 (token, head) rows x 32 keys, v_mfma_f32_16x16x32_bf16; probabilities
+ * rounded to bf16 for the P V product) and on the vector units for fp32.
  * Requires partition_size % block_size == 0, partition_size % 16 == 0 and
  * max_partitions*partition_size >= max_blocks_per_seq*block_size. */
 pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,

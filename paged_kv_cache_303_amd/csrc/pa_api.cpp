@@ -128,6 +128,7 @@ static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, 
   a->partition_size = 0;
   a->max_partitions = 1;
   a->waves_per_group = pa::waves_per_group(layout->num_kv_heads);
+  a->prefill_mfma = 0;
   return PA_OK;
 }
 
@@ -283,7 +284,11 @@ pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part
   a.part_lse = part_lse;
   a.partition_size = partition_size;
   a.max_partitions = max_partitions;
-  return pa::launch_status(pa::launch_decode(a, true, stream), what);
+  a.prefill_mfma = pa::prefill_mfma_supported(a) ? 1 : 0;
+  if (pa_status st = pa::launch_status(pa::launch_decode(a, true, stream), what)) return st;
+  if (a.prefill_mfma)
+    return pa::launch_status(pa::launch_prefill_mfma(a, stream), what);
+  return PA_OK;
 }
 
 pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const float* part_o,

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
   const int len = max(a.seq_lens[b], 0);
   const int key_end = len - q_len + (j - q_first) + 1;
   int nparts = 0;
-  if (key_end > 0) nparts = q_len > 1 ? 1 : (key_end + a.partition_size - 1) / a.partition_size;
+  if (key_end > 0) nparts = (key_end + a.partition_size - 1) / a.partition_size;
   nparts = min(nparts, a.max_partitions);
 
   const int D = a.head_dim;

@@ -489,12 +489,9 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
   const int key_end = len - q_len + (j - q_first) + 1;  // keys 0 .. position
   int start = 0, end = key_end;
   if constexpr (SPLIT) {
-    if (q_len > 1) {
-      if (part != 0) return;  // multi-query sequences: one partition
-    } else {
-      start = part * a.partition_size;
-      end = min(key_end, start + a.partition_size);
-    }
+    if (q_len > 1 && a.prefill_mfma) return;  // the MFMA prefill kernel takes these
+    start = part * a.partition_size;
+    end = min(key_end, start + a.partition_size);
     if (start >= end) return;  // this partition holds no key
   }
   using W = WaveCtx<T, D, G, UNIFORM>;

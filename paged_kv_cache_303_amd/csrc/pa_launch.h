@@ -32,6 +32,7 @@ struct DecodeArgs {
   int32_t partition_size;      // tokens per partition (split) or 0 (single pass)
   int32_t max_partitions;
   int32_t waves_per_group;     // KV heads (= waves) per workgroup
+  int32_t prefill_mfma;        // split: multi-query sequences go to the MFMA prefill kernel
 };
 
 struct ReduceArgs {
@@ -70,6 +71,10 @@ pa_status launch_decode(const DecodeArgs& a, bool split, void* stream);
 pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices);
 pa_status launch_decode_stream(const DecodeArgs& a, const StreamArgs& s, void* stream);
 pa_status launch_reduce(const ReduceArgs& a, void* stream);
+// Chunked-prefill tile on the matrix cores (bf16; cu_q_lens given): writes
+// partition 0 of every query token of the sequences with q_len > 1.
+bool prefill_mfma_supported(const DecodeArgs& a);
+pa_status launch_prefill_mfma(const DecodeArgs& a, void* stream);
 pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
                           const void* v_new, const int32_t* slots, int32_t num_tokens,
                           void* stream);

@@ -132,6 +132,46 @@ def test_chunked_prefill_small(pa, dtype):
     _check_all_paths(pa, w, st_p, st_o, partitions=(None, 16))
 
 
+@pytest.mark.parametrize("head_dim", [32, 64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_prefill_shape_grid(pa, head_dim, group):
+    """Prefill chunks (the matrix-core tile for bf16): row tiles cut mid-token,
+    several chunks and decode tokens in one launch, partitions of 48 keys
+    (not a multiple of the 32-key tile), block size 8."""
+    hkv = 2
+    w = wl.custom_decode(60 + head_dim + group, [70, 1, 130, 33, 200], num_blocks=256,
+                         block_size=8, num_q_heads=hkv * group, num_kv_heads=hkv,
+                         head_dim=head_dim, dtype=wl.BF16, q_lens=[70, 1, 37, 1, 65],
+                         partition_size=48, name=f"prefill_d{head_dim}_g{group}")
+    st_p, st_o = _both(pa, w)
+    _check_all_paths(pa, w, st_p, st_o, partitions=(None, 256))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_prefill_partials_match_oracle(pa, dtype):
+    """Every partition of every query (prefill chunks included) against the
+    oracle's per-partition summaries."""
+    binding, runner, _ = pa
+    w = wl.custom_decode(13, [100, 1, 64, 150], num_blocks=128, block_size=16,
+                         num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=dtype,
+                         q_lens=[100, 1, 3, 80], partition_size=32, name="prefill_partials")
+    st_p, st_o = _both(pa, w)
+    o_ref, lse_ref, nparts = orun.partials(w, st_o)
+    part_o, part_lse = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
+                                            st_p["block_tables"], st_p["seq_lens"], w.scale,
+                                            partition_size=w.partition_size,
+                                            cu_q_lens=st_p["cu_q_lens"])
+    po, pl = to_f64(part_o), to_f64(part_lse)
+    for j, n in enumerate(nparts):
+        if dtype == wl.F32:
+            np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=1e-5)
+            np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=1e-5)
+        else:  # bf16 probabilities in the matrix-core P V product
+            np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=5e-3)
+            d = np.abs(po[j, :, :n] - o_ref[j, :, :n])
+            assert (d <= 1e-2 + 2e-2 * np.abs(o_ref[j, :, :n])).all(), (j, d.max())
+
+
 # --- the five workloads ------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
