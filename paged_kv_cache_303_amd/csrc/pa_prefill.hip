@@ -21,12 +21,16 @@
 // K/V rows.  Keys go in tiles of 32:
 //   * the workgroup gathers the tile's K rows into LDS ([key][dim]) and its V
 //     rows transposed ([dim][key]), through the block table;
-//   * S = Q K^T with v_mfma_f32_16x16x32_bf16 (16 rows x 16 keys per
-//     instruction, 32 dims of the contraction per instruction);
-//   * online softmax per row in the log2 domain (running max, rescale of the
-//     running sum and of O when it moves), causal mask by position;
-//   * P is rounded to bf16 and staged through LDS into the A-operand layout,
-//     then O += P V with the same MFMA (K = the tile's 32 keys);
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (16 keys x 16 rows per
+//     instruction, 32 dims of the contraction per instruction): each lane
+//     then holds 8 scores of one query row, which are also the 8 values the
+//     A operand of P V needs for that row when the P V contraction runs over
+//     the keys in the same order (V^T is read in that order), so P stays in
+//     registers;
+//   * online softmax per row in the log2 domain with lazy rescaling (the
+//     running max moves only when a tile's exceeds it by more than 8), the
+//     causal and partition masks by position, probabilities rounded to bf16;
+//   * O += P V with the same MFMA, 32 keys of the tile per step;
 //   * the next tile's K/V rows are loaded into registers while the current
 //     one is computed.
 // MFMA operand layout (16x16x32): lane l holds A[l % 16][8 (l / 16) + e] and
@@ -43,12 +47,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kPfWaves = 4;             // waves per workgroup
 constexpr int kPfRows = 16 * kPfWaves;  // query rows per workgroup
-constexpr int kPfKeys = 32;             // keys per tile
+constexpr int kPfKeys = 32;             // keys per tile (a multiple of 32)
 constexpr int kPad = 8;                 // bf16 elements of padding per LDS row
 constexpr float kLn2Pf = 0.69314718055994530942f;
+constexpr float kPfLazy = 8.0f;  // running-max slack (log2 units) before a rescale
 constexpr int kPrefillMaxSeqs = 1024;   // sequences per launch (LDS prefix sums)
 constexpr int kPfMaxBlocks = 1024;      // block ids of one partition staged in LDS
-constexpr int kPfBlocksPerCu = 4;       // persistent workgroups per compute unit
+constexpr int kPfBlocksPerCu = 3;       // persistent workgroups per compute unit (all resident)
 
 __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -59,12 +64,6 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int D, int G>
 __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
     DecodeArgs a, const int32_t* __restrict__ block_tables) {
@@ -73,14 +72,12 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
   constexpr int CPR = D / 8;  // 16-byte chunks per K/V row
   constexpr int KS = D + kPad;        // LDS row stride of K (elements)
   constexpr int VS = kPfKeys + kPad;  // LDS row stride of V^T
-  constexpr int PS = kPfKeys + kPad;  // LDS row stride of P
   constexpr int NCH = kPfKeys * CPR;                          // 16-byte chunks of K per tile
   constexpr int NLD = (NCH + kPfWaves * kWave - 1) / (kPfWaves * kWave);  // per thread
   constexpr int NCHV = kPfKeys / 2 * CPR;                     // key-pair chunks of V per tile
   constexpr int NLDV = (NCHV + kPfWaves * kWave - 1) / (kPfWaves * kWave);
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPfKeys * KS];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VS];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[kPfWaves][16 * PS];
   __shared__ int wcum[kPrefillMaxSeqs + 1];  // prefix sums of work items per sequence
   __shared__ int blk_lds[kPfMaxBlocks];      // physical blocks of the item's key range
 
@@ -160,22 +157,19 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) qf[kk] = *(const uint4*)(qrow + 8 * (lane >> 4) + 32 * kk);
 
-    // rows this lane holds in the accumulator layout, and the last key each sees
-    int lim[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rc = min(row0 + 16 * w + 4 * (lane >> 4) + i, rows_total - 1);
-      lim[i] = min(pos_base + rc / G, k_hi - 1);
-    }
+    // Scores are computed transposed, S^T = K Q^T (K as the A operand, Q as
+    // B): lane l then holds the scores of one query row, l % 16, for keys
+    // 4 (l / 16) + i and 16 + 4 (l / 16) + i of the tile (i < 4) -- exactly
+    // the 8 contraction values the A operand of P V needs for that row, if
+    // the P V contraction runs over the keys in that order (V^T is read
+    // with the same order).  So P never leaves registers, and the softmax
+    // state is one row per lane (m, l), shared by the 4 lanes l % 16 == row.
+    const int rq = min(row0 + 16 * w + (lane & 15), rows_total - 1);  // this lane's row
+    const int lim = min(pos_base + rq / G, k_hi - 1);  // last key the row sees here
     const int wave_last = pos_base + min(q_len - 1, (row0 + 16 * w + 15) / G);
 
-    float m[4], l[4];
-    f32x4 o[DB];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-    }
+    float m = -INFINITY, l = 0.f;
+    f32x4 o[DB];  // O rows 4 (l / 16) + i, dim 16 db + l % 16
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -240,63 +234,71 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
       if (k0 + kPfKeys < k_hi) gather(k0 + kPfKeys);  // in flight during the compute
 
       if (k0 <= wave_last) {  // this wave has rows that see some key of the tile
-        // ---- S = Q K^T for two 16-key blocks ------------------------------
-        f32x4 s[2];
+        // ---- S^T = K Q^T for the tile's 16-key blocks ----------------------
+        constexpr int NB = kPfKeys / 16;  // 16-key blocks; pairs of them feed one P V step
+        f32x4 st[NB];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          s[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < NB; ++nb) {
+          st[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk) {
             const uint4 kf =
                 *(const uint4*)(k_lds + (nb * 16 + (lane & 15)) * KS + 8 * (lane >> 4) + 32 * kk);
-            s[nb] = mfma(qf[kk], kf, s[nb]);
+            st[nb] = mfma(kf, qf[kk], st[nb]);
           }
         }
-        // ---- online softmax per row (log2 domain), causal + partition mask --
-        float p[2][4];
+        // ---- online softmax of this lane's row (log2 domain), lazy rescale --
+        float x[NB * 4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float mx = -INFINITY;
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int key = k0 + nb * 16 + (lane & 15);
-            const float x = key <= lim[i] ? s[nb][i] * a.scale_log2 : -INFINITY;
-            p[nb][i] = x;
-            mx = fmaxf(mx, x);
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + nb * 16 + 4 * (lane >> 4) + i;
+            const float v = key <= lim ? st[nb][i] * a.scale_log2 : -INFINITY;
+            x[nb * 4 + i] = v;
+            mx = fmaxf(mx, v);
           }
-          mx = reduce_levels<0, 4>(mx, OpMax());  // across the 16 key lanes
-          const float m_new = fmaxf(m[i], mx);
-          const bool none = m_new == -INFINITY;  // row sees no key yet
-          const float alpha = none ? 1.f : fast_exp2(m[i] - m_new);
-          m[i] = m_new;
-          float sum = 0.f;
+        mx = reduce_levels<4, 6>(mx, OpMax());  // the 4 lanes of the row
+        // move the running max only when the tile's exceeds it by more than
+        // kPfLazy (probabilities then stay below 2^kPfLazy); the rescale of
+        // O needs each row's factor in the accumulator layout
+        const bool move = mx > m + kPfLazy;
+        if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+          const float m_new = move ? mx : m;
+          const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - m_new);
+          m = m_new;
+          l *= alpha;
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            // bf16 probabilities: the same values enter the sum and P V
-            const float pr = none ? 0.f : (float)(__bf16)fast_exp2(p[nb][i] - m_new);
-            p[nb][i] = pr;
-            sum += pr;
+          for (int i = 0; i < 4; ++i) {
+            const float ai = __shfl(alpha, 4 * (lane >> 4) + i, kWave);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db][i] *= ai;
           }
-          sum = reduce_levels<0, 4>(sum, OpSum());
-          l[i] = l[i] * alpha + sum;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[db][i] *= alpha;
         }
-        // ---- P (bf16) into the A-operand layout through LDS -----------------
-        uint16_t* pw = p_lds[w];
+        float sum = 0.f;
+        uint32_t pk[NB * 2];  // P as bf16 pairs, contraction order (block, i)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int e = 0; e < NB * 4; e += 2) {
+          const float p0 = m == -INFINITY ? 0.f : (float)(__bf16)fast_exp2(x[e] - m);
+          const float p1 = m == -INFINITY ? 0.f : (float)(__bf16)fast_exp2(x[e + 1] - m);
+          sum += p0 + p1;
+          pk[e / 2] = (uint32_t)bf16_bits(p0) | ((uint32_t)bf16_bits(p1) << 16);
+        }
+        l += reduce_levels<4, 6>(sum, OpSum());
+        // ---- O += P V: one MFMA step per pair of 16-key blocks; V^T rows read
+        //      in the same key order (keys 4g..4g+3, then 16+4g..16+4g+3) -------
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            pw[(4 * (lane >> 4) + i) * PS + nb * 16 + (lane & 15)] = bf16_bits(p[nb][i]);
-        wave_lds_sync();
-        const uint4 pf = *(const uint4*)(pw + (lane & 15) * PS + 8 * (lane >> 4));
-        // ---- O += P V --------------------------------------------------------
+        for (int h = 0; h < NB / 2; ++h) {
+          const uint4 pf = make_uint4(pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint4 vf =
-              *(const uint4*)(vt_lds + (db * 16 + (lane & 15)) * VS + 8 * (lane >> 4));
-          o[db] = mfma(pf, vf, o[db]);
+          for (int db = 0; db < DB; ++db) {
+            const uint16_t* vrow =
+                vt_lds + (db * 16 + (lane & 15)) * VS + 32 * h + 4 * (lane >> 4);
+            const uint2 v0 = *(const uint2*)vrow;
+            const uint2 v1 = *(const uint2*)(vrow + 16);
+            o[db] = mfma(pf, make_uint4(v0.x, v0.y, v1.x, v1.y), o[db]);
+          }
         }
       }
       __syncthreads();  // the next tile overwrites K, V^T
@@ -305,15 +307,17 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
     // ---- normalise and store this partition of each row that has keys in it --
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rc = row0 + 16 * w + 4 * (lane >> 4) + i;
+      const int src = 4 * (lane >> 4) + i;  // lane holding row `src`'s m and l
+      const float li = __shfl(l, src, kWave), mi = __shfl(m, src, kWave);
+      const int rc = row0 + 16 * w + src;
       if (rc >= rows_total || pos_base + rc / G < k_lo) continue;
       const int64_t jh = (int64_t)(q_first + rc / G) * a.num_q_heads + kvh * G + rc % G;
-      const float inv = 1.f / l[i];
+      const float inv = 1.f / li;
       float* po = a.part_o + (jh * a.max_partitions + part) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) po[db * 16 + (lane & 15)] = o[db][i] * inv;
       if ((lane & 15) == 0)
-        a.part_lse[jh * a.max_partitions + part] = (m[i] + __log2f(l[i])) * kLn2Pf;
+        a.part_lse[jh * a.max_partitions + part] = (mi + __log2f(li)) * kLn2Pf;
     }
   }
 }
