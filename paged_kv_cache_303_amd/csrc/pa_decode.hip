@@ -65,6 +65,9 @@ struct Elt<uint16_t> {  // bfloat16 bit patterns
 #ifndef PA_TILE_TOKENS
 #define PA_TILE_TOKENS 16  // target tokens per tile (per wave, per KV head)
 #endif
+#ifndef PA_MAX_CPL
+#define PA_MAX_CPL 2  // 16-byte chunks of a row per lane, at most
+#endif
 #ifndef PA_MAX_TILE_LOADS
 #define PA_MAX_TILE_LOADS 8  // 16-byte loads per lane per tile (K or V), hot shapes
 #endif
@@ -78,7 +81,7 @@ template <typename T, int D, int G, bool UNIFORM = true>
 struct Shape {
   static constexpr int VEC = Elt<T>::kVec;
   static constexpr int CHUNKS = D / VEC;
-  static constexpr int CPL = (CHUNKS >= 8 && G <= 4) ? 2 : 1;
+  static constexpr int CPL = (CHUNKS >= 8 && G <= 4 && PA_MAX_CPL >= 2) ? 2 : 1;
   static constexpr int LPR = CHUNKS / CPL;
   static constexpr int TPI = kWave / LPR;
   // Loads per lane per tile (K or V; two tiles are in registers at a time):
@@ -227,9 +230,9 @@ struct WaveCtx {
         const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kp + blk, (uint32_t)block_bytes);
         const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vp + blk, (uint32_t)block_bytes);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.k[i][k] = buffer_load16(kr, lane_off + k * kChunkStride, row);
+        for (int k = 0; k < CPL; ++k) tl.k[i][k] = buffer_load16_nt(kr, lane_off + k * kChunkStride, row);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16(vr, lane_off + k * kChunkStride, row);
+        for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16_nt(vr, lane_off + k * kChunkStride, row);
       }
     } else {
 #pragma unroll
@@ -240,9 +243,9 @@ struct WaveCtx {
         const char* kb = kp + phys * block_bytes + off;
         const char* vb = vp + phys * block_bytes + off;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.k[i][k] = *(const uint4*)(kb + k * kChunkStride);
+        for (int k = 0; k < CPL; ++k) tl.k[i][k] = load16_nt(kb + k * kChunkStride);
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.v[i][k] = *(const uint4*)(vb + k * kChunkStride);
+        for (int k = 0; k < CPL; ++k) tl.v[i][k] = load16_nt(vb + k * kChunkStride);
       }
     }
   }
@@ -537,24 +540,14 @@ __device__ __forceinline__ int64_t slice_start(int64_t r, int64_t T, int64_t R) 
 // An LDS value every lane reads at the same address, moved to a scalar register.
 __device__ __forceinline__ int uniform_lds(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
-// block_tables is a separate __restrict__ argument: nothing the kernel stores
-// can alias it, so its wave-uniform lookups stay scalar loads after stores.
-template <typename T, int D, int G, bool UNIFORM>
-__global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
-    DecodeArgs a, StreamArgs s, const int32_t* __restrict__ block_tables) {
-  using W = WaveCtx<T, D, G, UNIFORM>;
-  constexpr int TT = W::TT;
-  extern __shared__ int lds[];
+// Prefix sums of tiles per sequence into LDS: ends[b] = len_b (clamped to the
+// table's capacity), cum[b] = tiles of sequences 0..b-1 (TT tokens a tile).
+// Every thread loads lengths (one memory round trip), wave 0 scans.  Ends
+// with a workgroup barrier.
+template <int TT>
+__device__ void tile_prefix(const DecodeArgs& a, int* cum, int* ends) {
   const int B = a.num_seqs;
-  int* cum = lds;            // [B + 1]
-  int* ends = lds + B + 1;   // [B]
-  const int groups = a.num_kv_heads / a.waves_per_group;
-  const int r = blockIdx.x / groups;
-  const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
   const int cap = a.max_blocks << a.log2_bs;
-
-  // ---- prefix sums of tiles per sequence -------------------------------------
-  // every thread loads lengths (one memory round trip), wave 0 scans in LDS
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
     const int len = min(max(a.seq_lens[i], 0), cap);
     ends[i] = len;
@@ -578,6 +571,34 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
     }
   }
   __syncthreads();
+}
+
+// The last b with cum[b] <= t (cum in LDS, non-decreasing, cum[0] = 0 <= t).
+__device__ __forceinline__ int seq_of_tile(const int* cum, int B, int64_t t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (uniform_lds(&cum[mid]) <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// block_tables is a separate __restrict__ argument: nothing the kernel stores
+// can alias it, so its wave-uniform lookups stay scalar loads after stores.
+template <typename T, int D, int G, bool UNIFORM>
+__global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
+    DecodeArgs a, StreamArgs s, const int32_t* __restrict__ block_tables) {
+  using W = WaveCtx<T, D, G, UNIFORM>;
+  constexpr int TT = W::TT;
+  extern __shared__ int lds[];
+  const int B = a.num_seqs;
+  int* cum = lds;            // [B + 1]
+  int* ends = lds + B + 1;   // [B]
+  const int groups = a.num_kv_heads / a.waves_per_group;
+  const int r = blockIdx.x / groups;
+  const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
+
+  tile_prefix<TT>(a, cum, ends);
   const int64_t total = uniform_lds(&cum[B]);
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= B; i += blockDim.x) s.cum[i] = cum[i];
@@ -586,13 +607,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   const int64_t t_end = slice_start(r + 1, total, s.num_slices);
   if (t_begin >= t_end) return;
 
-  // first sequence of the slice: the last b with cum[b] <= t_begin
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uniform_lds(&cum[mid]) <= t_begin) lo = mid; else hi = mid - 1;
-  }
-  const int b_first = lo;
+  const int b_first = seq_of_tile(cum, B, t_begin);  // first sequence of the slice
 
   __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
   W w(a, kvh, q_lds[wave_id()]);
@@ -668,18 +683,30 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(Decod
   float o[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane + 64 * i
   for (int k0 = 0; k0 < nseg; k0 += kWave) {
     const int k = k0 + lane;
-    const int64_t idx = k < nseg ? seg_index(k) : -1;
+    const int idx = k < nseg ? (int)seg_index(k) : -1;
     const float wgt = idx >= 0 ? __expf(s.part_lse[idx] - m) : 0.f;
     den += wgt;
     const int n = min(kWave, nseg - k0);
-    for (int q = 0; q < n; ++q) {  // slices of this chunk, weights from lane q
-      const float wq = __shfl(wgt, q, kWave);
-      const int64_t iq = __shfl((long long)idx, q, kWave);
-      if (iq < 0) continue;
-      const float* po = s.part_o + iq * D;
+    // slices of this group, four at a time so that their rows load together:
+    // weight and partial row index from lane q (scalars).  Empty slices and
+    // lanes past the group read row 0 and select the value away (the row may
+    // hold anything, NaN included: it is never multiplied in)
+    for (int q0 = 0; q0 < n; q0 += 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (lane + i * kWave < D) o[i] = fmaf(wq, po[lane + i * kWave], o[i]);
+      for (int u = 0; u < 4; ++u) {
+        const int q = q0 + u;  // <= 63: n <= 64 and q0 is a multiple of 4
+        const float wq = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), q));
+        const int iraw = __builtin_amdgcn_readlane(idx, q);
+        const bool used = iraw >= 0;
+        const float* po = s.part_o + (int64_t)(used ? iraw : 0) * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (lane + i * kWave < D) {
+            const float x = po[lane + i * kWave];
+            o[i] = used ? fmaf(wq, x, o[i]) : o[i];
+          }
+      }
     }
   }
   den = reduce_levels<0, 6>(den, OpSum());

@@ -143,6 +143,26 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Cache-policy operand of buffer instructions on gfx950: the non-temporal
+// (nt) bit.  Streaming data that is read exactly once is loaded with it so
+// that it does not displace reusable lines; measured on MI355X, a permuted
+// 32 KiB-block read of 1.7 GB rises from 6.2 to 7.0 TB/s with it.
+constexpr int kCachePolicyNT = 2;
+
+// The same load, non-temporal.
+__device__ __forceinline__ uint4 buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                  uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kCachePolicyNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 16-byte non-temporal load through a flat global pointer.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // 2^x on the transcendental unit; exact 0 for x = -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
