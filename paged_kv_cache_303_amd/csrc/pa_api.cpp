@@ -153,7 +153,7 @@ pa_status stream_layout(const pa::DecodeArgs& a, StreamLayout* sl) {
   sl->slices = slices;
   sl->o_bytes = align256((size_t)slices * 2 * a.num_q_heads * a.head_dim * sizeof(float));
   sl->lse_bytes = align256((size_t)slices * 2 * a.num_q_heads * sizeof(float));
-  sl->cum_bytes = align256((size_t)(a.num_seqs + 1) * sizeof(int32_t));
+  sl->cum_bytes = align256((size_t)a.num_seqs * 4 * sizeof(int32_t));
   return PA_OK;
 }
 
@@ -238,7 +238,7 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const 
       pa::StreamArgs s;
       s.part_o = (float*)ws;
       s.part_lse = (float*)(ws + sl.o_bytes);
-      s.cum = (int32_t*)(ws + sl.o_bytes + sl.lse_bytes);
+      s.seq_slices = (int32_t*)(ws + sl.o_bytes + sl.lse_bytes);
       s.num_slices = sl.slices;
       return pa::launch_status(pa::launch_decode_stream(a, s, stream), what);
     }

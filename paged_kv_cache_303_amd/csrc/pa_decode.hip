@@ -600,12 +600,26 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
 
   tile_prefix<TT>(a, cum, ends);
   const int64_t total = uniform_lds(&cum[B]);
+  // slices actually used: at most one per tile, so none is empty
+  const int64_t R = min((int64_t)s.num_slices, total);
   if (blockIdx.x == 0) {
-    for (int i = threadIdx.x; i <= B; i += blockDim.x) s.cum[i] = cum[i];
+    // for the merge kernel, per sequence: the slices holding its first and
+    // last tile (the largest r with slice_start(r) <= t), and whether the
+    // first of them begins with an earlier sequence (partial slot 1)
+    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+      const int64_t c0 = cum[i], c1 = cum[i + 1];
+      int4 v = make_int4(-1, -1, 0, 0);
+      if (c0 < c1) {
+        const int64_t r1 = ((c0 + 1) * R - 1) / total;
+        const int64_t r2 = (c1 * R - 1) / total;
+        v = make_int4((int)r1, (int)r2, slice_start(r1, total, R) < c0 ? 1 : 0, 0);
+      }
+      ((int4*)s.seq_slices)[i] = v;
+    }
   }
-  const int64_t t_begin = slice_start(r, total, s.num_slices);
-  const int64_t t_end = slice_start(r + 1, total, s.num_slices);
-  if (t_begin >= t_end) return;
+  if (r >= R) return;
+  const int64_t t_begin = slice_start(r, total, R);
+  const int64_t t_end = slice_start(r + 1, total, R);
 
   const int b_first = seq_of_tile(cum, B, t_begin);  // first sequence of the slice
 
@@ -639,8 +653,12 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
 
 // Merge the partials of every sequence cut by slice boundaries; zero rows for
 // sequences without keys.  One wave per (sequence, head), kFixupWaves heads
-// per workgroup; lane s handles the s-th slice of the sequence (64 at a time).
+// per workgroup.  The sequence's slice range comes precomputed from the
+// streaming kernel, so the partial rows of its first kPre slices are loaded
+// together with the lse values (one memory round trip); lane k handles the
+// k-th slice's weight, every lane its columns of the weighted sum.
 constexpr int kFixupWaves = 4;
+constexpr int kPre = 8;
 
 __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(DecodeArgs a,
                                                                           StreamArgs s) {
@@ -649,57 +667,69 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(Decod
   if (h >= a.num_q_heads) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int D = a.head_dim;
-  const int64_t T = s.cum[a.num_seqs];
-  const int64_t c0 = s.cum[b], c1 = s.cum[b + 1];
-  const int64_t R = s.num_slices;
   const bool bf16 = a.dtype == PA_BF16;
   const int64_t row = (int64_t)b * a.num_q_heads + h;
-  if (c0 == c1) {  // no key: zero row
+  const int4 sv = ((const int4*)s.seq_slices)[b];
+  const int r1 = __builtin_amdgcn_readfirstlane(sv.x);
+  const int r2 = __builtin_amdgcn_readfirstlane(sv.y);
+  const bool first_cut = __builtin_amdgcn_readfirstlane(sv.z) != 0;
+  if (r1 < 0) {  // no key: zero row
     for (int d = lane; d < D; d += kWave) {
       if (bf16) ((uint16_t*)a.out)[row * D + d] = 0;
       else ((float*)a.out)[row * D + d] = 0.f;
     }
     return;
   }
-  // slice holding tile t: the largest r with slice_start(r) <= t
-  const int64_t r1 = ((c0 + 1) * R - 1) / T;
-  const int64_t r2 = (c1 * R - 1) / T;
   if (r1 == r2) return;  // wholly inside one slice: already written
-  const int nseg = (int)(r2 - r1 + 1);
-  // partial index of slice r1 + k, or -1 for an empty slice
-  auto seg_index = [&](int k) -> int64_t {
-    const int64_t r = r1 + k;
-    if (slice_start(r, T, R) == slice_start(r + 1, T, R)) return -1;
-    const int slot = (k == 0 && slice_start(r1, T, R) < c0) ? 1 : 0;
-    return (r * 2 + slot) * a.num_q_heads + h;
+  const int nseg = r2 - r1 + 1;
+  // partial row of slice r1 + k (slot 1 if the slice began with an earlier sequence)
+  auto seg_index = [&](int k) -> int {
+    const int slot = (k == 0 && first_cut) ? 1 : 0;
+    return ((r1 + k) * 2 + slot) * a.num_q_heads + h;
   };
-  float m = -INFINITY;
-  for (int k = lane; k < nseg; k += kWave) {
-    const int64_t idx = seg_index(k);
-    if (idx >= 0) m = fmaxf(m, s.part_lse[idx]);
+  // rows of the first kPre slices (slices past the sequence re-read slice 0's
+  // row and get weight 0 below)
+  float pre[kPre][4];
+#pragma unroll
+  for (int q = 0; q < kPre; ++q) {
+    const float* po = s.part_o + (int64_t)seg_index(q < nseg ? q : 0) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pre[q][i] = lane + i * kWave < D ? po[lane + i * kWave] : 0.f;
   }
+  float m = -INFINITY;
+  for (int k = lane; k < nseg; k += kWave) m = fmaxf(m, s.part_lse[seg_index(k)]);
   m = reduce_levels<0, 6>(m, OpMax());
   float den = 0.f;
   float o[4] = {0.f, 0.f, 0.f, 0.f};  // dims lane + 64 * i
   for (int k0 = 0; k0 < nseg; k0 += kWave) {
     const int k = k0 + lane;
-    const int idx = k < nseg ? (int)seg_index(k) : -1;
-    const float wgt = idx >= 0 ? __expf(s.part_lse[idx] - m) : 0.f;
+    const bool valid = k < nseg;
+    const int idx = seg_index(valid ? k : 0);
+    const float wgt = valid ? __expf(s.part_lse[idx] - m) : 0.f;
     den += wgt;
     const int n = min(kWave, nseg - k0);
-    // slices of this group, four at a time so that their rows load together:
-    // weight and partial row index from lane q (scalars).  Empty slices and
-    // lanes past the group read row 0 and select the value away (the row may
-    // hold anything, NaN included: it is never multiplied in)
-    for (int q0 = 0; q0 < n; q0 += 4) {
+    int q0 = 0;
+    if (k0 == 0) {  // the preloaded rows (weight 0 past the sequence)
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        const float wq = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), q));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(wq, pre[q][i], o[i]);
+      }
+      q0 = kPre;
+    }
+    // the rest, four slices at a time so that their rows load together;
+    // slots past the sequence read row 0 and select the value away
+    for (; q0 < n; q0 += 4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int q = q0 + u;  // <= 63: n <= 64 and q0 is a multiple of 4
+        const bool used = q < n;
         const float wq = __builtin_bit_cast(
             float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), q));
-        const int iraw = __builtin_amdgcn_readlane(idx, q);
-        const bool used = iraw >= 0;
-        const float* po = s.part_o + (int64_t)(used ? iraw : 0) * D;
+        const int iq = __builtin_amdgcn_readlane(idx, q);
+        const float* po = s.part_o + (int64_t)(used ? iq : 0) * D;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (lane + i * kWave < D) {

@@ -55,8 +55,10 @@ struct ReduceArgs {
 struct StreamArgs {
   float* part_o;       // [num_slices, 2, num_q_heads, head_dim]
   float* part_lse;     // [num_slices, 2, num_q_heads]
-  int32_t* cum;        // [num_seqs + 1] prefix sums of tiles per sequence
-  int32_t num_slices;  // equal slices of the batch's (sequence, tile) work
+  int32_t* seq_slices; // [num_seqs, 4]: first and last slice holding the sequence's
+                       // tiles (-1: no key), whether the first slice begins with an
+                       // earlier sequence, 0
+  int32_t num_slices;  // equal slices of the batch's (sequence, tile) work (at most)
 };
 
 // Sequences the streaming decode handles per launch (its LDS holds two ints
