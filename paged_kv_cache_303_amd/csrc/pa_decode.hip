@@ -524,14 +524,15 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
 // ---------------------------------------------------------------------------
 // Balanced streaming decode (one query token per sequence).
 //
-// All (sequence, tile) pairs are laid end to end -- sequence b contributes
-// tiles(b) = ceil(len_b / TT) -- and cut into R equal slices, one per
-// workgroup slot that is resident on the device at once; the KV-head groups
-// of a slice are consecutive workgroups.  A workgroup computes the prefix sums
-// cum[] of tiles(b) in LDS, walks its slice, writes the output of every
-// sequence that lies wholly inside the slice, and stores (o, lse) for a
-// sequence that the slice cuts: slot 0 if it is the slice's first sequence,
-// slot 1 if it is its last.  stream_fixup_kernel merges the cut sequences.
+// The batch's work is laid end to end -- sequence b contributes its tiles,
+// tiles(b) = ceil(len_b / TT), plus a fixed restart cost (kSeqCost units) --
+// and cut into R equal slices, one per workgroup slot that is resident on the
+// device at once (at most one per unit); the KV-head groups of a slice are
+// consecutive workgroups.  A workgroup computes the prefix sums cum[] of the
+// units in LDS, walks its slice, writes the output of every sequence whose
+// tiles lie wholly inside the slice, and stores (o, lse) for a sequence that
+// the slice cuts: slot 0 if it is the slice's first sequence, slot 1 if it is
+// its last.  stream_fixup_kernel merges the cut sequences.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t slice_start(int64_t r, int64_t T, int64_t R) {
   return r * T / R;
@@ -540,18 +541,32 @@ __device__ __forceinline__ int64_t slice_start(int64_t r, int64_t T, int64_t R) 
 // An LDS value every lane reads at the same address, moved to a scalar register.
 __device__ __forceinline__ int uniform_lds(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
-// Prefix sums of tiles per sequence into LDS: ends[b] = len_b (clamped to the
-// table's capacity), cum[b] = tiles of sequences 0..b-1 (TT tokens a tile).
-// Every thread loads lengths (one memory round trip), wave 0 scans.  Ends
-// with a workgroup barrier.
+// Work units of a sequence in the balanced decode's static slicing: its tiles
+// plus kSeqCost units for the pipeline restart at every sequence a slice
+// holds (query load, first block-table lookups and gathers, and the final
+// cross-lane combine and store).  Per-wave timestamps on MI355X put one
+// restart at 5-7 us, two to three tiles' time; a sweep of kSeqCost over
+// 0..6 on the batch-256 GQA decode is fastest at 4 (2% below 0).  The extra
+// units come first: sequence b occupies units [cum[b], cum[b+1]), its tiles
+// are the last tiles(b) of them, and an empty sequence has none.
+#ifndef PA_SEQ_COST
+#define PA_SEQ_COST 4
+#endif
+constexpr int kSeqCost = PA_SEQ_COST;
+
+// Prefix sums of work units per sequence into LDS: ends[b] = len_b (clamped
+// to the table's capacity), cum[b] = units of sequences 0..b-1 (TT tokens a
+// tile).  Every thread loads lengths (one memory round trip), wave 0 scans.
+// Ends with a workgroup barrier.
 template <int TT>
 __device__ void tile_prefix(const DecodeArgs& a, int* cum, int* ends) {
   const int B = a.num_seqs;
   const int cap = a.max_blocks << a.log2_bs;
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
     const int len = min(max(a.seq_lens[i], 0), cap);
+    const int tiles = (len + TT - 1) / TT;
     ends[i] = len;
-    cum[i + 1] = (len + TT - 1) / TT;
+    cum[i + 1] = tiles > 0 ? tiles + kSeqCost : 0;
   }
   __syncthreads();
   if (threadIdx.x < kWave) {
@@ -605,14 +620,16 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   if (blockIdx.x == 0) {
     // for the merge kernel, per sequence: the slices holding its first and
     // last tile (the largest r with slice_start(r) <= t), and whether the
-    // first of them begins with an earlier sequence (partial slot 1)
+    // first of them begins before the sequence's units, i.e. with tiles of
+    // an earlier sequence (partial slot 1)
     for (int i = threadIdx.x; i < B; i += blockDim.x) {
-      const int64_t c0 = cum[i], c1 = cum[i + 1];
+      const int64_t u0 = cum[i], u1 = cum[i + 1];
       int4 v = make_int4(-1, -1, 0, 0);
-      if (c0 < c1) {
-        const int64_t r1 = ((c0 + 1) * R - 1) / total;
-        const int64_t r2 = (c1 * R - 1) / total;
-        v = make_int4((int)r1, (int)r2, slice_start(r1, total, R) < c0 ? 1 : 0, 0);
+      if (u0 < u1) {
+        const int64_t first = u0 + kSeqCost;  // unit of the first tile
+        const int64_t r1 = ((first + 1) * R - 1) / total;
+        const int64_t r2 = (u1 * R - 1) / total;
+        v = make_int4((int)r1, (int)r2, slice_start(r1, total, R) < u0 ? 1 : 0, 0);
       }
       ((int4*)s.seq_slices)[i] = v;
     }
@@ -628,17 +645,18 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   for (int b = b_first; b < B; ++b) {
     const int c_lo = uniform_lds(&cum[b]);
     const int c_hi = uniform_lds(&cum[b + 1]);
-    const int64_t seg_lo = max(t_begin, (int64_t)c_lo);
+    const int t_lo = c_hi > c_lo ? c_lo + kSeqCost : c_lo;  // unit of the first tile
+    const int64_t seg_lo = max(t_begin, (int64_t)t_lo);
     const int64_t seg_hi = min(t_end, (int64_t)c_hi);
     if (seg_lo < seg_hi) {
-      const int start = (int)(seg_lo - c_lo) * TT;
-      const int stop = min(uniform_lds(&ends[b]), (int)(seg_hi - c_lo) * TT);
+      const int start = (int)(seg_lo - t_lo) * TT;
+      const int stop = min(uniform_lds(&ends[b]), (int)(seg_hi - t_lo) * TT);
       w.load_query(b);
       w.reset();
       w.run(block_tables + (int64_t)b * a.max_blocks, start, stop);
       float l[G];
       w.combine(l);
-      if (seg_lo == c_lo && seg_hi == c_hi) {
+      if (seg_lo == t_lo && seg_hi == c_hi) {
         w.store_out(a.out, b, l);
       } else {
         const int slot = (b == b_first) ? 0 : 1;
