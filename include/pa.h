@@ -33,9 +33,9 @@
  *     [0, num_blocks) and seq_lens in [0, max_blocks_per_seq*block_size].
  *     Violations give unspecified results, but the kernels clamp every index
  *     they derive from device data, so no access leaves the arrays passed.
- *   - Supported shapes: dtype PA_F32 or PA_BF16; head_dim 32, 64, 128 or
- *     256; block_size a power of two from 1 to 256; num_q_heads /
- *     num_kv_heads in {1, 2, 4, 8}.
+ *   - Supported shapes: dtype PA_F32, PA_BF16 or PA_FP8; head_dim 32, 64,
+ *     128 or 256 (PA_FP8: 64, 128 or 256); block_size a power of two from 1
+ *     to 256; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  *   - Softmax scores are scale * dot(q, k) with a finite scale > 0; every
  *     workload passes 1/sqrt(head_dim), the value the pages use.
  */
@@ -58,7 +58,12 @@ typedef enum {
   PA_ERR_NOT_FOUND = 5       /* unknown sequence handle */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* Pool element types.  PA_FP8: e4m3 codes (1 byte: sign, 4 exponent bits of
+ * bias 7, 3 mantissa bits; largest finite 448; 0x7F/0xFF are NaN) with one
+ * float32 scale per (token, KV head) in separate scale pools
+ * [num_blocks, block_size, num_kv_heads]; the stored value is code * scale.
+ * Queries and outputs of fp8 pools are bfloat16. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
 /* Shape of the two KV pools (K and V share it): [num_blocks, block_size,
  * num_kv_heads, head_dim] elements of `dtype`.  "19.2 KV Cache 系统化管理"
@@ -130,6 +135,40 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q,
  * the workspace is ignored). */
 pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
                                    int32_t num_q_heads, size_t* bytes);
+
+/* FP8 KV cache ("19.2 KV Cache 系统化管理" §19.2.4, KV Cache 量化压缩: every
+ * token's K and V vectors are scaled and quantized on their own, and
+ * dequantized by multiplying the scale back; the page's formula is lost, the
+ * reading here is symmetric absmax).  layout->dtype must be PA_FP8; k_pool
+ * and v_pool hold e4m3 codes [num_blocks, block_size, num_kv_heads,
+ * head_dim], k_scale and v_scale float32 [num_blocks, block_size,
+ * num_kv_heads], all caller-owned device memory.
+ *
+ * Quantizing cache write: for every token t with slot s = slot_mapping[t]
+ * in [0, num_blocks*block_size) and every KV head, the row x (head_dim
+ * values of k_new / v_new, bfloat16 [num_tokens, num_kv_heads, head_dim])
+ * gets scale = max|x| / 448 and codes e4m3(x / scale) (float32 division,
+ * clamped to +-448, nearest even; scale 0 and zero codes for a zero row),
+ * stored at row s of the pools.  Other slots are skipped. */
+pa_status pa_kv_write_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                          float* k_scale, float* v_scale, const void* k_new, const void* v_new,
+                          const int32_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/* Paged decode over fp8 pools: as pa_decode, with key and value rows read as
+ * code * scale.  q and out are bfloat16 [num_seqs, num_q_heads, head_dim];
+ * the workspace is sized by pa_decode_workspace_size with the same layout. */
+pa_status pa_decode_fp8(const pa_kv_layout* layout, void* out, const void* q,
+                        const void* k_pool, const void* v_pool, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Copy-on-write of fp8 pools: as pa_copy_blocks, for the codes and the
+ * scales of every (src, dst) pair. */
+pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                             float* k_scale, float* v_scale, const int32_t* pairs,
+                             int32_t num_pairs, void* stream);
 
 /* Split-sequence paged attention, first pass.  The keys a query sees are cut
  * into partitions of `partition_size` tokens (partition p = keys

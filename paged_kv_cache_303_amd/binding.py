@@ -24,7 +24,7 @@ from . import build as _build
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_NO_FREE_BLOCKS, PA_ERR_HIP, \
     PA_ERR_NOT_FOUND = range(6)
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8 = 0, 1, 2
 
 
 class PagedAttentionError(RuntimeError):
@@ -57,6 +57,10 @@ _SIGNATURES = {
     "pa_decode": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p,
                          ctypes.c_size_t, _p]),
     "pa_decode_workspace_size": (_i32, [_LAYOUT, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pa_kv_write_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _p, _p, _i32, _p]),
+    "pa_decode_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
+                             _p, ctypes.c_size_t, _p]),
+    "pa_copy_blocks_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p]),
     "pa_decode_split": (_i32, [_LAYOUT, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p,
                                _i32, _i32, _f32, _p]),
     "pa_reduce": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]),
@@ -111,7 +115,9 @@ def _check(status: int) -> None:
 
 # --- device calls -------------------------------------------------------------
 
-_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+# fp8 pools hold e4m3 codes: uint8 tensors (or torch's float8_e4m3fn, the same bytes)
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.uint8: PA_FP8,
+           torch.float8_e4m3fn: PA_FP8}
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None) -> ctypes.c_void_p:
@@ -167,6 +173,62 @@ def copy_blocks(k_pool, v_pool, pairs) -> None:
         raise ValueError("pairs must be [n, 2]")
     _check(lib().pa_copy_blocks(ctypes.byref(lay), kp, vp, _dev(pairs, "pairs", torch.int32),
                                 int(pairs.shape[0]), _stream()))
+
+
+def _fp8_pools(k_pool, v_pool, k_scale, v_scale):
+    lay, kp, vp = _pools(k_pool, v_pool)
+    if lay.dtype != PA_FP8:
+        raise TypeError("fp8 pools are uint8 (e4m3 codes)")
+    shape = tuple(k_pool.shape[:3])
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
+    return lay, kp, vp, _dev(k_scale, "k_scale", torch.float32), \
+        _dev(v_scale, "v_scale", torch.float32)
+
+
+def kv_write_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping) -> None:
+    """``pa_kv_write_fp8``: quantize bf16 rows ``new[t]`` into slot ``slot_mapping[t]``."""
+    lay, kp, vp, ks, vs = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    n = int(slot_mapping.shape[0])
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if tuple(t.shape) != (n, lay.num_kv_heads, lay.head_dim):
+            raise ValueError(f"{name} must be [num_tokens, num_kv_heads, head_dim]")
+    _check(lib().pa_kv_write_fp8(ctypes.byref(lay), kp, vp, ks, vs,
+                                 _dev(k_new, "k_new", torch.bfloat16),
+                                 _dev(v_new, "v_new", torch.bfloat16),
+                                 _dev(slot_mapping, "slot_mapping", torch.int32), n, _stream()))
+
+
+def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, pairs) -> None:
+    """``pa_copy_blocks_fp8``: codes and scales of block src copied to dst."""
+    lay, kp, vp, ks, vs = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2]")
+    _check(lib().pa_copy_blocks_fp8(ctypes.byref(lay), kp, vp, ks, vs,
+                                    _dev(pairs, "pairs", torch.int32), int(pairs.shape[0]),
+                                    _stream()))
+
+
+def decode_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, scale: float,
+               out=None, workspace=None):
+    """``pa_decode_fp8``: decode over e4m3 pools; bf16 ``q`` and output.  Returns ``out``."""
+    lay, kp, vp, ks, vs = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    if q.dim() != 3 or q.shape[2] != lay.head_dim:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    bt, mb, sl = _tables(block_tables, seq_lens, b)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    ws, ws_bytes = ctypes.c_void_p(0), 0
+    if workspace is not None:
+        ws, ws_bytes = _dev(workspace, "workspace", torch.uint8), workspace.numel()
+    _check(lib().pa_decode_fp8(ctypes.byref(lay), _dev(out, "out", torch.bfloat16),
+                               _dev(q, "q", torch.bfloat16), kp, vp, ks, vs, bt, mb, sl, b, hq,
+                               float(scale), ws, ws_bytes, _stream()))
+    return out
 
 
 def _tables(block_tables, seq_lens, num_seqs):

@@ -34,13 +34,19 @@ int32_t log2i(int32_t x) {
   return r;
 }
 
+// Bytes of one pool element.
+int64_t elt_bytes(int32_t dtype) { return dtype == PA_BF16 ? 2 : (dtype == PA_FP8 ? 1 : 4); }
+
 // Checks the pool layout; `what` names the calling entry point.
 pa_status check_layout(const pa_kv_layout* l, const char* what) {
   if (!l) return fail(PA_ERR_INVALID_ARG, "%s: layout is NULL", what);
   if (l->num_blocks <= 0 || l->block_size <= 0 || l->num_kv_heads <= 0 || l->head_dim <= 0)
     return fail(PA_ERR_INVALID_ARG, "%s: layout sizes must be positive", what);
-  if (l->dtype != PA_F32 && l->dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not PA_F32 or PA_BF16", what, l->dtype);
+  if (l->dtype != PA_F32 && l->dtype != PA_BF16 && l->dtype != PA_FP8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d is not PA_F32, PA_BF16 or PA_FP8", what,
+                l->dtype);
+  if (l->dtype == PA_FP8 && l->head_dim < 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools need head_dim >= 64", what);
   if (!pow2(l->block_size) || l->block_size > 256)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d is not a power of two <= 256", what,
                 l->block_size);
@@ -51,7 +57,7 @@ pa_status check_layout(const pa_kv_layout* l, const char* what) {
   if (rows > (int64_t)INT32_MAX + 1)
     return fail(PA_ERR_INVALID_ARG, "%s: num_blocks*block_size exceeds the int32 slot range", what);
   const int64_t block_bytes =
-      (int64_t)l->block_size * l->num_kv_heads * l->head_dim * (l->dtype == PA_BF16 ? 2 : 4);
+      (int64_t)l->block_size * l->num_kv_heads * l->head_dim * elt_bytes(l->dtype);
   if (block_bytes > (int64_t)1 << 30)
     return fail(PA_ERR_UNSUPPORTED, "%s: one block exceeds 1 GiB", what);
   return PA_OK;
@@ -108,6 +114,8 @@ static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, 
   a->q = q;
   a->k_pool = k_pool;
   a->v_pool = v_pool;
+  a->k_scale = nullptr;
+  a->v_scale = nullptr;
   a->block_tables = block_tables;
   a->seq_lens = seq_lens;
   a->cu_q_lens = nullptr;
@@ -170,6 +178,8 @@ pa_status pa_kv_write(const pa_kv_layout* layout, void* k_pool, void* v_pool, co
                       void* stream) {
   const char* what = "pa_kv_write";
   if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (layout->dtype == PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools are written by pa_kv_write_fp8", what);
   if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", what);
   if (num_tokens == 0) return PA_OK;
   if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping)
@@ -183,11 +193,14 @@ pa_status pa_copy_blocks(const pa_kv_layout* layout, void* k_pool, void* v_pool,
                          const int32_t* pairs, int32_t num_pairs, void* stream) {
   const char* what = "pa_copy_blocks";
   if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (layout->dtype == PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools (codes and scales) use pa_copy_blocks_fp8",
+                what);
   if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
   if (num_pairs == 0) return PA_OK;
   if (!k_pool || !v_pool || !pairs) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
   const int64_t block_bytes = (int64_t)layout->block_size * layout->num_kv_heads *
-                              layout->head_dim * (layout->dtype == PA_BF16 ? 2 : 4);
+                              layout->head_dim * pa::elt_bytes(layout->dtype);
   if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
   return pa::launch_status(
@@ -211,17 +224,12 @@ pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
   return PA_OK;
 }
 
-pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const void* k_pool,
-                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
-                    void* workspace, size_t workspace_bytes, void* stream) {
-  const char* what = "pa_decode";
-  pa::DecodeArgs a;
-  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
-                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
-                                      &a))
-    return st;
-  if (num_seqs == 0) return PA_OK;
+}  // extern "C"
+
+// pa_decode / pa_decode_fp8 after their own argument checks.
+static pa_status decode_launch(const char* what, pa::DecodeArgs& a, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (a.num_seqs == 0) return PA_OK;
   if (!out) return fail(PA_ERR_INVALID_ARG, "%s: out is NULL", what);
   a.out = out;
   if (workspace != nullptr) {
@@ -246,6 +254,87 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const 
   return pa::launch_status(pa::launch_decode(a, false, stream), what);
 }
 
+extern "C" {
+
+pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const void* k_pool,
+                    const void* v_pool, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "pa_decode";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (layout->dtype == PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools need their scales: use pa_decode_fp8", what);
+  return decode_launch(what, a, out, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_fp8(const pa_kv_layout* layout, void* out, const void* q,
+                        const void* k_pool, const void* v_pool, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t num_q_heads, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* what = "pa_decode_fp8";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (layout->dtype != PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout dtype must be PA_FP8", what);
+  if (num_seqs > 0 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL scale pool", what);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return decode_launch(what, a, out, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_kv_write_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                          float* k_scale, float* v_scale, const void* k_new, const void* v_new,
+                          const int32_t* slot_mapping, int32_t num_tokens, void* stream) {
+  const char* what = "pa_kv_write_fp8";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (layout->dtype != PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout dtype must be PA_FP8", what);
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_tokens < 0", what);
+  if (num_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !k_new || !v_new || !slot_mapping)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  return pa::launch_status(pa::launch_kv_write_fp8(*layout, k_pool, v_pool, k_scale, v_scale,
+                                                   k_new, v_new, slot_mapping, num_tokens,
+                                                   stream),
+                           what);
+}
+
+pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,
+                             float* k_scale, float* v_scale, const int32_t* pairs,
+                             int32_t num_pairs, void* stream) {
+  const char* what = "pa_copy_blocks_fp8";
+  if (pa_status st = pa::check_layout(layout, what)) return st;
+  if (layout->dtype != PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout dtype must be PA_FP8", what);
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_scale || !v_scale || !pairs)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  const int64_t block_bytes =
+      (int64_t)layout->block_size * layout->num_kv_heads * layout->head_dim;
+  if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
+  // the codes, then the scales as a pool of float32 rows of num_kv_heads
+  if (pa_status st = pa::launch_status(
+          pa::launch_copy_blocks(*layout, k_pool, v_pool, pairs, num_pairs, stream), what))
+    return st;
+  pa_kv_layout sc = *layout;
+  sc.head_dim = 1;
+  sc.dtype = PA_F32;
+  return pa::launch_status(
+      pa::launch_copy_blocks(sc, k_scale, v_scale, pairs, num_pairs, stream), what);
+}
+
 pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,
                           int32_t max_partitions, int32_t partition_size, const void* q,
                           const int32_t* cu_q_lens, int32_t num_q_tokens, const void* k_pool,
@@ -258,6 +347,8 @@ pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part
                                       max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
                                       &a))
     return st;
+  if (layout->dtype == PA_FP8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools are decoded by pa_decode_fp8", what);
   if (num_q_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_q_tokens < 0", what);
   if (!cu_q_lens && num_q_tokens != num_seqs)
     return fail(PA_ERR_INVALID_ARG,

@@ -9,6 +9,8 @@
 // * copy_blocks (same page, §19.2.2): pool[dst] = pool[src], K and V; a block
 //   is one contiguous span of block_size rows.  Workgroups stride over
 //   (pair, 16 KiB chunk) so a handful of pairs still fills the chip.
+// * kv_write_fp8 (same page, §19.2.4): the quantizing write into e4m3 pools
+//   with one scale per (token, KV head).
 // * reduce: the partitions of one query head are merged with weights
 //   exp(lse_p - L), L = log sum_p exp(lse_p) -- the online-softmax rescale of
 //   §19.2.3 applied once per partition.
@@ -37,6 +39,44 @@ __global__ __launch_bounds__(256) void kv_write_kernel(char* __restrict__ kp, ch
     dk[i] = a;
     dv[i] = b;
   }
+}
+
+// Quantizing write into e4m3 pools ("19.2 KV Cache 系统化管理" §19.2.4: every
+// token's vector is scaled on its own).  One wave per (token, KV head, K|V):
+// the row's absmax across the wave, scale = absmax / 448, codes of x / scale
+// (IEEE float32 division, clamped to +-448) by the hardware's nearest-even
+// conversion; lane i handles the value pairs 2i + 128k.  A zero row gets
+// scale 0 and zero codes.
+__global__ __launch_bounds__(64) void kv_write_fp8_kernel(
+    uint8_t* __restrict__ kp, uint8_t* __restrict__ vp, float* __restrict__ ks,
+    float* __restrict__ vs, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
+    const int32_t* __restrict__ slots, int32_t num_kv_heads, int32_t head_dim, int64_t num_rows) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_rows) return;
+  const int lane = threadIdx.x;
+  const uint16_t* x = (is_v ? vn : kn) + ((int64_t)t * num_kv_heads + h) * head_dim;
+  uint8_t* dst = (is_v ? vp : kp) + (s * num_kv_heads + h) * head_dim;
+  float amax = 0.f;
+  for (int d = 2 * lane; d < head_dim; d += 2 * kWave) {
+    const uint32_t pair = *(const uint32_t*)(x + d);
+    amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(pair)), fabsf(bf16_hi(pair))));
+  }
+  amax = reduce_levels<0, 6>(amax, OpMax());
+  const float scale = __fdiv_rn(amax, 448.f);
+  for (int d = 2 * lane; d < head_dim; d += 2 * kWave) {
+    const uint32_t pair = *(const uint32_t*)(x + d);
+    uint32_t codes = 0;
+    if (scale > 0.f) {
+      const float a = fminf(fmaxf(__fdiv_rn(bf16_lo(pair), scale), -448.f), 448.f);
+      const float b = fminf(fmaxf(__fdiv_rn(bf16_hi(pair), scale), -448.f), 448.f);
+      codes = f32x2_to_fp8(a, b);
+    }
+    *(uint16_t*)(dst + d) = (uint16_t)codes;
+  }
+  if (lane == 0) (is_v ? vs : ks)[s * num_kv_heads + h] = scale;
 }
 
 constexpr int64_t kCopyChunk = 16384;  // bytes per workgroup
@@ -127,7 +167,9 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
     a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
 }
 
-inline int64_t elt_size(int32_t dtype) { return dtype == PA_BF16 ? 2 : 4; }
+inline int64_t elt_size(int32_t dtype) {
+  return dtype == PA_BF16 ? 2 : (dtype == PA_FP8 ? 1 : 4);
+}
 
 }  // namespace
 
@@ -141,6 +183,18 @@ pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, con
   hipLaunchKernelGGL(kv_write_kernel, dim3(num_tokens), dim3(threads), 0, (hipStream_t)stream,
                      (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new, slots,
                      row_bytes, num_rows);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_kv_write_fp8(const pa_kv_layout& l, void* k_pool, void* v_pool, float* k_scale,
+                              float* v_scale, const void* k_new, const void* v_new,
+                              const int32_t* slots, int32_t num_tokens, void* stream) {
+  if (num_tokens == 0) return PA_OK;
+  const int64_t num_rows = (int64_t)l.num_blocks * l.block_size;
+  hipLaunchKernelGGL(kv_write_fp8_kernel, dim3(num_tokens, l.num_kv_heads, 2), dim3(kWave), 0,
+                     (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool, k_scale, v_scale,
+                     (const uint16_t*)k_new, (const uint16_t*)v_new, slots, l.num_kv_heads,
+                     l.head_dim, num_rows);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

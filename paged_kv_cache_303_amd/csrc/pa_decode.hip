@@ -61,6 +61,10 @@ template <>
 struct Elt<uint16_t> {  // bfloat16 bit patterns
   static constexpr int kVec = 8;
 };
+template <>
+struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
+  static constexpr int kVec = 16;
+};
 
 #ifndef PA_TILE_TOKENS
 #define PA_TILE_TOKENS 16  // target tokens per tile (per wave, per KV head)
@@ -81,14 +85,15 @@ template <typename T, int D, int G, bool UNIFORM = true>
 struct Shape {
   static constexpr int VEC = Elt<T>::kVec;
   static constexpr int CHUNKS = D / VEC;
-  static constexpr int CPL = (CHUNKS >= 8 && G <= 4 && PA_MAX_CPL >= 2) ? 2 : 1;
+  // (fp8: one chunk of 16 codes per lane already needs 16 accumulators per head)
+  static constexpr int CPL = (CHUNKS >= 8 && G <= 4 && PA_MAX_CPL >= 2 && sizeof(T) > 1) ? 2 : 1;
   static constexpr int LPR = CHUNKS / CPL;
   static constexpr int TPI = kWave / LPR;
   // Loads per lane per tile (K or V; two tiles are in registers at a time):
   // the bf16 shapes with small G get the full budget, the others less, so
   // that accumulators and both tiles stay in 256 VGPRs without spilling.
   static constexpr int MAX_LOADS =
-      (sizeof(T) == 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
+      (sizeof(T) <= 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
       : (G >= 8 ? PA_MAX_TILE_LOADS / 4 : PA_MAX_TILE_LOADS / 2);
   static constexpr int NI0 = (PA_TILE_TOKENS / TPI) < 1 ? 1 : (PA_TILE_TOKENS / TPI);
   static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
@@ -117,17 +122,22 @@ struct WaveCtx {
   static constexpr int VEC = S::VEC, CPL = S::CPL, LPR = S::LPR, LOG_LPR = ilog2(S::LPR);
   static constexpr int TPI = S::TPI, NI = S::NI, TT = S::TT;
   static constexpr bool BF16 = sizeof(T) == 2;
+  // fp8 pools: e4m3 codes with one fp32 scale per (token, KV head) for K and
+  // V; the query and the output are bfloat16
+  static constexpr bool FP8 = sizeof(T) == 1;
   static constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
+  static constexpr int QW = FP8 ? 2 : 1;  // 16-byte query pieces per chunk
 
   struct Tile {
     uint4 k[NI][CPL];
     uint4 v[NI][CPL];
+    float ks[FP8 ? NI : 1], vs[FP8 ? NI : 1];  // fp8: scales of the lane's rows
   };
 
-  // The current query lives in LDS, not registers: [G][CPL][LPR] 16-byte
-  // chunks per wave (fp32: pre-scaled), read back once per tile; the lanes
+  // The current query lives in LDS, not registers: [G][CPL][LPR][QW] 16-byte
+  // pieces per wave (fp32: pre-scaled), read back once per tile; the lanes
   // of one chunk column read the same address (broadcast).
-  static constexpr int kQChunks = G * CPL * LPR;
+  static constexpr int kQChunks = G * CPL * LPR * QW;
 
   const DecodeArgs& a;
   uint4* qs;  // this wave's kQChunks chunks in LDS
@@ -148,12 +158,29 @@ struct WaveCtx {
     lane_col = (uint32_t)(kvh * D + c * VEC) * sizeof(T);
     nb_max = a.num_blocks - 1;
     bs_mask = (1 << a.log2_bs) - 1;
-    qk_scale = BF16 ? a.scale_log2 : 1.0f;
+    qk_scale = (BF16 || FP8) ? a.scale_log2 : 1.0f;  // fp32 queries are pre-scaled
   }
 
   // Query token j's chunks of the G heads into LDS; scores stay unscaled and
   // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
   __device__ void load_query(int j) {
+    if constexpr (FP8) {  // bf16 query: a chunk's 16 dims are two 16-byte pieces
+      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
+      if (tg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int k = 0; k < CPL; ++k)
+#pragma unroll
+            for (int h = 0; h < QW; ++h)
+              qs[((g * CPL + k) * LPR + c) * QW + h] =
+                  *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC + h * 8);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      return;
+    }
     const T* qrow = (const T*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
     if (tg == 0) {
 #pragma unroll
@@ -233,6 +260,12 @@ struct WaveCtx {
         for (int k = 0; k < CPL; ++k) tl.k[i][k] = buffer_load16_nt(kr, lane_off + k * kChunkStride, row);
 #pragma unroll
         for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16_nt(vr, lane_off + k * kChunkStride, row);
+        if constexpr (FP8) {  // this lane's row: tg rows into the instruction's rows
+          const int64_t srow =
+              ((int64_t)phys << a.log2_bs) + ((t0 + i * TPI) & bs_mask) + tg;
+          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
+          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
+        }
       }
     } else {
 #pragma unroll
@@ -246,6 +279,11 @@ struct WaveCtx {
         for (int k = 0; k < CPL; ++k) tl.k[i][k] = load16_nt(kb + k * kChunkStride);
 #pragma unroll
         for (int k = 0; k < CPL; ++k) tl.v[i][k] = load16_nt(vb + k * kChunkStride);
+        if constexpr (FP8) {
+          const int64_t srow = ((int64_t)phys << a.log2_bs) + (tok & bs_mask);
+          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
+          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
+        }
       }
     }
   }
@@ -262,6 +300,27 @@ struct WaveCtx {
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
+        if constexpr (FP8) {  // 16 bf16 query values against 16 e4m3 codes
+          const uint4 q0 = qs[((g * CPL + k) * LPR + c) * QW];
+          const uint4 q1 = qs[((g * CPL + k) * LPR + c) * QW + 1];
+          const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+          float qf[16];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            qf[2 * e] = bf16_lo(qw[e]);
+            qf[2 * e + 1] = bf16_hi(qw[e]);
+          }
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            float kf[16];
+            fp8x16_to_f32(tl.k[i][k], kf);
+            float d = s[i][g];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) d = fmaf(qf[e], kf[e], d);
+            s[i][g] = d;
+          }
+          continue;
+        }
         const uint4 qv = qs[(g * CPL + k) * LPR + c];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -285,6 +344,12 @@ struct WaveCtx {
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int g = 0; g < G; ++g) s[i][g] = reduce_levels<0, LOG_LPR>(s[i][g], OpSum());
+    if constexpr (FP8) {  // the row's K scale (rows past the end are selected away below)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[i][g] *= tl.ks[i];
+    }
     const bool tail = t0 + TT > end;
     if (tail) {  // rows past the end get probability 0
 #pragma unroll
@@ -330,6 +395,28 @@ struct WaveCtx {
     }
 
     // ---- PV --------------------------------------------------------------------
+    if constexpr (FP8) {  // p * (code * scale): the row's V scale goes into p
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float vsc = tl.vs[i];
+        const bool valid = !(UNIFORM && tail) || (t0 + i * TPI + tg) < end;
+        vsc = valid ? vsc : 0.f;  // masked rows may hold NaN poison: select, never multiply
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          float vf[16];
+          fp8x16_to_f32(tl.v[i][k], vf);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) vf[e] = valid ? vf[e] : 0.f;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pv = s[i][g] * vsc;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[g][k][e] = fmaf(pv, vf[e], acc[g][k][e]);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -398,6 +485,28 @@ struct WaveCtx {
   // Normalised output of query j (dtype T) -- after combine().
   __device__ void store_out(void* out, int j, const float (&l)[G]) const {
     if (tg != 0) return;
+    if constexpr (FP8) {  // bf16 output, 16 dims a chunk
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float inv = 1.f / l[g];
+        uint16_t* o = (uint16_t*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int col = (c + k * LPR) * VEC;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float* x = &acc[g][k][8 * h];
+            uint4 w;
+            w.x = pack_bf16x2(x[0] * inv, x[1] * inv);
+            w.y = pack_bf16x2(x[2] * inv, x[3] * inv);
+            w.z = pack_bf16x2(x[4] * inv, x[5] * inv);
+            w.w = pack_bf16x2(x[6] * inv, x[7] * inv);
+            *(uint4*)(o + col + 8 * h) = w;
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float inv = 1.f / l[g];
@@ -443,6 +552,17 @@ struct WaveCtx {
 
   __device__ void store_zero(void* out, int j) const {
     if (tg != 0) return;
+    if constexpr (FP8) {  // bf16 output
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *(uint4*)((uint16_t*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D +
+                      (c + k * LPR) * VEC + 8 * h) = make_uint4(0, 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -685,7 +805,7 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(Decod
   if (h >= a.num_q_heads) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int D = a.head_dim;
-  const bool bf16 = a.dtype == PA_BF16;
+  const bool bf16 = a.dtype != PA_F32;  // bf16 output for bf16 and fp8 pools
   const int64_t row = (int64_t)b * a.num_q_heads + h;
   const int4 sv = ((const int4*)s.seq_slices)[b];
   const int r1 = __builtin_amdgcn_readfirstlane(sv.x);
@@ -847,7 +967,11 @@ pa_status dispatch(const DecodeArgs& a, F&& f) {
   };
   auto by_d = [&](auto t) -> pa_status {
     switch (a.head_dim) {
-      case 32: return by_g(t, std::integral_constant<int, 32>());
+      case 32:
+        // fp8 rows of 32 codes would put 32 tokens in one load instruction,
+        // more than the 16-token alignment of partitions and slices
+        if constexpr (sizeof(decltype(t)) == 1) return PA_ERR_UNSUPPORTED;
+        else return by_g(t, std::integral_constant<int, 32>());
       case 64: return by_g(t, std::integral_constant<int, 64>());
       case 128: return by_g(t, std::integral_constant<int, 128>());
       case 256: return by_g(t, std::integral_constant<int, 256>());
@@ -856,6 +980,7 @@ pa_status dispatch(const DecodeArgs& a, F&& f) {
   };
   if (a.dtype == PA_BF16) return by_d(uint16_t());
   if (a.dtype == PA_F32) return by_d(float());
+  if (a.dtype == PA_FP8) return by_d(uint8_t());
   return PA_ERR_UNSUPPORTED;
 }
 

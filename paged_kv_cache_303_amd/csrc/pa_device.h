@@ -163,6 +163,31 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// ---------------------------------------------------------------------------
+// e4m3 (fp8) codes: the hardware's packed conversions on gfx950 use the e4m3
+// format with bias 7, maximum 448, NaN 0x7F/0xFF, rounding to nearest even.
+// ---------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The 16 codes of a 16-byte chunk as floats, in memory order.
+__device__ __forceinline__ void fp8x16_to_f32(const uint4& w, float (&f)[16]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], false);
+    const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)u[i], true);
+    f[4 * i] = lo[0];
+    f[4 * i + 1] = lo[1];
+    f[4 * i + 2] = hi[0];
+    f[4 * i + 3] = hi[1];
+  }
+}
+
+// Two floats to two e4m3 codes (low byte = a), nearest even.
+__device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
 // 2^x on the transcendental unit; exact 0 for x = -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -12,6 +12,8 @@ struct DecodeArgs {
   const void* q;               // [num_q_tokens, num_q_heads, head_dim]
   const void* k_pool;          // [num_blocks, block_size, num_kv_heads, head_dim]
   const void* v_pool;
+  const float* k_scale;        // fp8 pools: [num_blocks, block_size, num_kv_heads] scales
+  const float* v_scale;        //   (nullptr for fp32 / bf16 pools)
   const int32_t* block_tables; // [num_seqs, max_blocks]
   const int32_t* seq_lens;     // [num_seqs]
   const int32_t* cu_q_lens;    // [num_seqs + 1] or nullptr (one query per sequence)
@@ -80,6 +82,10 @@ pa_status launch_prefill_mfma(const DecodeArgs& a, void* stream);
 pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
                           const void* v_new, const int32_t* slots, int32_t num_tokens,
                           void* stream);
+// Quantizing cache write into e4m3 pools (bf16 new tokens).
+pa_status launch_kv_write_fp8(const pa_kv_layout& l, void* k_pool, void* v_pool, float* k_scale,
+                              float* v_scale, const void* k_new, const void* v_new,
+                              const int32_t* slots, int32_t num_tokens, void* stream);
 pa_status launch_copy_blocks(const pa_kv_layout& l, void* k_pool, void* v_pool,
                              const int32_t* pairs, int32_t num_pairs, void* stream);
 

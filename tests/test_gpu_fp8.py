@@ -1,0 +1,174 @@
+"""GPU parity of the FP8 (e4m3) KV cache ("19.2 KV Cache 系统化管理" §19.2.4).
+
+Every workload's tokens go through ``pa_kv_write_fp8`` into e4m3 pools with
+per-(token, KV head) scales, and through the oracle's quantization into its
+own pools.  Codes and scales are compared bit for bit (pools NaN-poisoned
+beforehand, so untouched rows must stay poison on both sides).  Decode over
+the fp8 pools (grid and balanced paths) is compared with the oracle's
+attention over its own dequantized pools, to the bf16 tolerance: both sides
+read the same code * scale values, so what remains is fp32 accumulation
+order and the bf16 rounding of the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import quant as oq
+from oracle import runner as orun
+from oracle.attention import bf16_bits_to_f64, paged_attention
+from paged_kv_cache_303_amd import workloads as wl
+from tests.parity import check_attention
+
+pytestmark = pytest.mark.gpu
+
+NAN_CODE = 0x7F
+
+
+@pytest.fixture(scope="module")
+def pa(built_library, gpu):
+    from paged_kv_cache_303_amd import binding, runner
+    return binding, runner, gpu
+
+
+def _slots(log):
+    return np.concatenate([np.asarray(s, np.int32) for _, s, _ in log]).astype(np.int32)
+
+
+def _gpu_fp8(pa, w, st):
+    binding, runner, dev = pa
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = torch.full(shape, NAN_CODE, dtype=torch.uint8, device=dev)
+    vc = torch.full(shape, NAN_CODE, dtype=torch.uint8, device=dev)
+    ks = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    vs = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    slots = torch.from_numpy(_slots(st["log"])).to(dev)
+    binding.kv_write_fp8(kc, vc, ks, vs, runner.to_device(w.k_tokens, "bf16", dev),
+                         runner.to_device(w.v_tokens, "bf16", dev), slots)
+    return kc, vc, ks, vs
+
+
+def _oracle_fp8(w, st_o):
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = np.full(shape, NAN_CODE, np.uint8)
+    vc = np.full(shape, NAN_CODE, np.uint8)
+    ks = np.full(shape[:3], np.nan, np.float32)
+    vs = np.full(shape[:3], np.nan, np.float32)
+    k_new = bf16_bits_to_f64(w.k_tokens).astype(np.float32)  # exact widening
+    v_new = bf16_bits_to_f64(w.v_tokens).astype(np.float32)
+    oq.kv_write_fp8(kc, vc, ks, vs, k_new, v_new, _slots(st_o["log"]), w.block_size)
+    return kc, vc, ks, vs
+
+
+def _run(pa, w, tokens=None):
+    binding, runner, dev = pa
+    assert w.dtype == wl.BF16 and w.cu_q_lens is None
+    print(f"[case] fp8 {w.name} B={len(w.decode_seqs)} heads={w.num_q_heads}/{w.num_kv_heads} "
+          f"d={w.head_dim} bs={w.block_size}", flush=True)
+    st = runner.replay(w, dev, poison=False)
+    st_o = orun.replay(w, with_pools=False)
+    np.testing.assert_array_equal(st["block_tables_host"], st_o["block_tables"])
+    g = _gpu_fp8(pa, w, st)
+    o = _oracle_fp8(w, st_o)
+    torch.cuda.synchronize()
+    # codes and scales: bit for bit (poisoned rows included)
+    for name, gt, ot in zip(("k codes", "v codes"), g[:2], o[:2]):
+        assert np.array_equal(gt.cpu().numpy(), ot), name
+    for name, gt, ot in zip(("k scales", "v scales"), g[2:], o[2:]):
+        assert np.array_equal(gt.cpu().numpy().view(np.uint32), ot.view(np.uint32)), name
+    ref = paged_attention(w.q, oq.dequantize(o[0], o[2]), oq.dequantize(o[1], o[3]),
+                          st_o["block_tables"], st_o["seq_lens"], w.scale, w.block_size,
+                          tokens=tokens)
+    args = (st["q"], g[0], g[1], g[2], g[3], st["block_tables"], st["seq_lens"], w.scale)
+    stats = {"grid": check_attention(binding.decode_fp8(*args), ref, "bf16", tokens,
+                                     f"{w.name} fp8 grid")}
+    ws = binding.decode_workspace(g[0], len(w.seq_lens), w.num_q_heads)
+    if ws is not None:
+        stats["balanced"] = check_attention(binding.decode_fp8(*args, workspace=ws), ref, "bf16",
+                                            tokens, f"{w.name} fp8 balanced")
+    print(f"[parity] {w.name} fp8: " + ", ".join(f"{k} max_err={v[0]:.2e} rel={v[1]:.2e}"
+                                                  for k, v in stats.items()), flush=True)
+    return stats
+
+
+LENS = [1, 2, 3, 15, 16, 17, 31, 33, 64, 100, 257, 600]
+
+
+@pytest.mark.parametrize("head_dim", [64, 128, 256])
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_fp8_shape_grid(pa, head_dim, group):
+    hkv = 2
+    w = wl.custom_decode(300 + head_dim + group, LENS, num_blocks=256, block_size=16,
+                         num_q_heads=hkv * group, num_kv_heads=hkv, head_dim=head_dim,
+                         dtype=wl.BF16, name=f"fp8_d{head_dim}_g{group}")
+    _run(pa, w)
+
+
+@pytest.mark.parametrize("block_size", [1, 4, 8, 32])
+def test_fp8_block_sizes(pa, block_size):
+    # block sizes below the rows of one load instruction take the per-lane lookup path
+    w = wl.custom_decode(400 + block_size, LENS, num_blocks=2048 // block_size + 64,
+                         block_size=block_size, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                         dtype=wl.BF16, name=f"fp8_bs{block_size}")
+    _run(pa, w)
+
+
+def test_fp8_gqa_batch(pa):
+    w = wl.gqa_decode(seed=5, batch=48, median=400, hi=3000, num_blocks=4096)
+    w.name = "fp8_gqa_b48"
+    _run(pa, w)
+
+
+def test_fp8_zero_rows_and_empty_sequence(pa):
+    binding, runner, dev = pa
+    w = wl.custom_decode(7, [5, 3, 9], num_blocks=16, block_size=4, num_q_heads=4,
+                         num_kv_heads=2, head_dim=64, dtype=wl.BF16, name="fp8_zero")
+    w.k_tokens[:3] = 0  # whole zero rows: scale 0, zero codes
+    st = runner.replay(w, dev, poison=False)
+    g = _gpu_fp8(pa, w, st)
+    st_o = orun.replay(w, with_pools=False)
+    o = _oracle_fp8(w, st_o)
+    assert np.array_equal(g[0].cpu().numpy(), o[0])
+    assert np.array_equal(g[2].cpu().numpy().view(np.uint32), o[2].view(np.uint32))
+    assert (o[2][o[2] == o[2]] == 0).sum() >= 3 * w.num_kv_heads  # the zero rows: scale 0
+    lens = st["seq_lens"].clone()
+    lens[1] = 0  # a sequence without keys gives a zero row
+    for ws in (None, binding.decode_workspace(g[0], 3, w.num_q_heads)):
+        out = binding.decode_fp8(st["q"], g[0], g[1], g[2], g[3], st["block_tables"], lens,
+                                 w.scale, workspace=ws)
+        assert torch.equal(out[1].float().cpu(), torch.zeros_like(out[1].float().cpu()))
+        assert torch.isfinite(out.float()).all()
+
+
+def test_fp8_copy_blocks(pa):
+    binding, runner, dev = pa
+    shape = (8, 16, 2, 64)
+    gen = torch.Generator().manual_seed(0)
+    kc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)
+    vc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)
+    ks = torch.rand(shape[:3], generator=gen).to(dev)
+    vs = torch.rand(shape[:3], generator=gen).to(dev)
+    k0, v0, ks0, vs0 = kc.clone(), vc.clone(), ks.clone(), vs.clone()
+    pairs = torch.tensor([[1, 5], [2, 6]], dtype=torch.int32, device=dev)
+    binding.copy_blocks_fp8(kc, vc, ks, vs, pairs)
+    torch.cuda.synchronize()
+    for s, d in [(1, 5), (2, 6)]:
+        assert torch.equal(kc[d], k0[s]) and torch.equal(vc[d], v0[s])
+        assert torch.equal(ks[d], ks0[s]) and torch.equal(vs[d], vs0[s])
+    for b in [0, 1, 2, 3, 4, 7]:
+        assert torch.equal(kc[b], k0[b]) and torch.equal(ks[b], ks0[b])
+
+
+def test_fp8_rejections(pa):
+    binding, runner, dev = pa
+    k = torch.zeros((4, 16, 2, 32), dtype=torch.uint8, device=dev)
+    s = torch.zeros((4, 16, 2), dtype=torch.float32, device=dev)
+    q = torch.zeros((1, 4, 32), dtype=torch.bfloat16, device=dev)
+    bt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
+    sl = torch.ones((1,), dtype=torch.int32, device=dev)
+    with pytest.raises(binding.PagedAttentionError):  # fp8 needs head_dim >= 64
+        binding.decode_fp8(q, k, k, s, s, bt, sl, 0.1)
+    k64 = torch.zeros((4, 16, 2, 64), dtype=torch.uint8, device=dev)
+    with pytest.raises(binding.PagedAttentionError):  # plain pa_decode refuses fp8 pools
+        binding.decode(torch.zeros((1, 4, 64), dtype=torch.uint8, device=dev), k64, k64, bt, sl,
+                       0.1)
