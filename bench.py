@@ -23,6 +23,9 @@ Reported:
                  events around it on the launch stream, against 8 TB/s;
                  `traffic` is filled from rocprofv3 counters when they were
                  taken for this kernel version (see --traffic)
+  fp8_kv         the same batch decoded from an FP8 (e4m3) cache with
+                 per-(token, KV head) scales (pa_kv_write_fp8 + pa_decode_fp8):
+                 decode time, effective GB/s of codes + scales, queries/s
   cpu_baseline   the CPU oracle (float64 NumPy, single thread) timed on a
                  bounded sample of the same queries (seeded order, ~15 s)
 
@@ -153,6 +156,8 @@ def main():
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / args.steps
 
+    fp8 = _fp8_decode(binding, runner, w, st, slots, q, bt_d, sl_d, args, dev)
+
     if args.calib_copy_mib > 0:
         _calibration_copy(binding, k_pool, v_pool, args.calib_copy_mib, dev)
 
@@ -201,6 +206,7 @@ def main():
             "ms": round(split_ms, 4),
             "kv_GBps": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1),
         },
+        "fp8_kv": fp8,
         "roofline": {
             "kernel": "pa_decode (decode_stream_kernel<bf16,128,4> + stream_fixup_kernel)",
             "bound": "hbm",
@@ -216,6 +222,48 @@ def main():
     if args.cpu_budget > 0:
         result["cpu_baseline"] = _cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)
+
+
+def _fp8_decode(binding, runner, w, st, new_slots, q, bt_d, sl_d, args, dev):
+    """The same batch from an FP8 (e4m3) cache: every token quantized into e4m3 pools
+    with per-(token, KV head) scales, then the balanced decode over them (timed)."""
+    import numpy as np
+    import torch
+
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    vc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    ks = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    vs = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    ctx = np.concatenate([np.asarray(sl, np.int32) for _, sl, _ in st["log"]])
+    all_slots = torch.from_numpy(np.concatenate([ctx, new_slots]).astype(np.int32)).to(dev)
+    binding.kv_write_fp8(kc, vc, ks, vs, runner.to_device(w.k_tokens, w.dtype, dev),
+                         runner.to_device(w.v_tokens, w.dtype, dev), all_slots)
+    ws = binding.decode_workspace(kc, len(w.seq_lens), w.num_q_heads)
+    out = torch.empty_like(q)
+    for _ in range(args.warmup):
+        binding.decode_fp8(q, kc, vc, ks, vs, bt_d, sl_d, w.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        binding.decode_fp8(q, kc, vc, ks, vs, bt_d, sl_d, w.scale, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tokens = int(sum(w.seq_lens))
+    code_bytes = tokens * w.num_kv_heads * w.head_dim * 2        # K and V codes
+    scale_bytes = tokens * w.num_kv_heads * 4 * 2                # K and V scales
+    del kc, vc, ks, vs
+    return {
+        "format": "e4m3 codes + one fp32 scale per (token, KV head), bf16 q/out",
+        "decode_ms": round(ms, 4),
+        "kv_bytes": code_bytes + scale_bytes,
+        "kv_GBps": round((code_bytes + scale_bytes) / (ms * 1e-3) / 1e9, 1),
+        "pct_hbm_peak": round(100.0 * (code_bytes + scale_bytes) / (ms * 1e-3) / 1e9
+                              / HBM_PEAK_GBPS, 2),
+        "queries_per_s": round(len(w.seq_lens) / (ms * 1e-3), 1),
+    }
 
 
 def _long_context(args):
