@@ -69,6 +69,9 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 #ifndef PA_TILE_TOKENS
 #define PA_TILE_TOKENS 16  // target tokens per tile (per wave, per KV head)
 #endif
+#ifndef PA_FP8_TILE_TOKENS
+#define PA_FP8_TILE_TOKENS 32  // the same for e4m3 pools (half the bytes per row)
+#endif
 #ifndef PA_MAX_CPL
 #define PA_MAX_CPL 2  // 16-byte chunks of a row per lane, at most
 #endif
@@ -95,7 +98,8 @@ struct Shape {
   static constexpr int MAX_LOADS =
       (sizeof(T) <= 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
       : (G >= 8 ? PA_MAX_TILE_LOADS / 4 : PA_MAX_TILE_LOADS / 2);
-  static constexpr int NI0 = (PA_TILE_TOKENS / TPI) < 1 ? 1 : (PA_TILE_TOKENS / TPI);
+  static constexpr int TILE_TOKENS = sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : PA_TILE_TOKENS;
+  static constexpr int NI0 = (TILE_TOKENS / TPI) < 1 ? 1 : (TILE_TOKENS / TPI);
   static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
   static constexpr int TT = NI * TPI;
   // Ranges start at multiples of 16 (partitions) or of TT (slices), plus
@@ -126,7 +130,11 @@ struct WaveCtx {
   // V; the query and the output are bfloat16
   static constexpr bool FP8 = sizeof(T) == 1;
   static constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
-  static constexpr int QW = FP8 ? 2 : 1;  // 16-byte query pieces per chunk
+  static constexpr int QW = FP8 ? 2 : 1;  // 16-byte pieces of one chunk of the bf16 query
+  // fp8 with up to 4 heads per KV head and head_dim <= 128: the query in
+  // registers (see qf); otherwise in LDS like the other types (registers
+  // would not hold it)
+  static constexpr bool QREG = FP8 && G <= 4 && D <= 128;
 
   struct Tile {
     uint4 k[NI][CPL];
@@ -134,10 +142,11 @@ struct WaveCtx {
     float ks[FP8 ? NI : 1], vs[FP8 ? NI : 1];  // fp8: scales of the lane's rows
   };
 
-  // The current query lives in LDS, not registers: [G][CPL][LPR][QW] 16-byte
-  // pieces per wave (fp32: pre-scaled), read back once per tile; the lanes
-  // of one chunk column read the same address (broadcast).
-  static constexpr int kQChunks = G * CPL * LPR * QW;
+  // The current query lives in LDS, not registers: [G][CPL][LPR] 16-byte
+  // chunks per wave (fp32: pre-scaled), read back once per tile; the lanes
+  // of one chunk column read the same address (broadcast).  (fp8: registers,
+  // see qf.)
+  static constexpr int kQChunks = QREG ? 1 : G * CPL * LPR * QW;
 
   const DecodeArgs& a;
   uint4* qs;  // this wave's kQChunks chunks in LDS
@@ -147,6 +156,10 @@ struct WaveCtx {
   int nb_max, bs_mask;
   float qk_scale;
   float m_run[G], l_run[G], acc[G][CPL][VEC];
+  // fp8: the current query's 16 dims of this lane's chunk, per head, as floats
+  // (held in registers for the whole sequence: each K chunk is converted once
+  // per tile and dotted with all G heads)
+  float qf[QREG ? G : 1][QREG ? 16 : 1];
 
   __device__ WaveCtx(const DecodeArgs& args, int kv_head, uint4* q_lds)
       : a(args), qs(q_lds), kvh(kv_head) {
@@ -164,17 +177,31 @@ struct WaveCtx {
   // Query token j's chunks of the G heads into LDS; scores stay unscaled and
   // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
   __device__ void load_query(int j) {
-    if constexpr (FP8) {  // bf16 query: a chunk's 16 dims are two 16-byte pieces
+    if constexpr (QREG) {  // bf16 query: every lane widens its chunk's 16 dims per head
+      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int h = 0; h < QW; ++h) {
+          const uint4 v = *(const uint4*)(qrow + (int64_t)g * D + c * VEC + h * 8);
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qf[g][8 * h + 2 * e] = bf16_lo(w[e]);
+            qf[g][8 * h + 2 * e + 1] = bf16_hi(w[e]);
+          }
+        }
+      return;
+    }
+    if constexpr (FP8) {  // bf16 query in LDS: a chunk's 16 dims are two 16-byte pieces
       const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
       if (tg == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int k = 0; k < CPL; ++k)
-#pragma unroll
-            for (int h = 0; h < QW; ++h)
-              qs[((g * CPL + k) * LPR + c) * QW + h] =
-                  *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC + h * 8);
+          for (int h = 0; h < QW; ++h)
+            qs[((g * CPL) * LPR + c) * QW + h] =
+                *(const uint4*)(qrow + (int64_t)g * D + c * VEC + h * 8);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -296,31 +323,46 @@ struct WaveCtx {
     for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int g = 0; g < G; ++g) s[i][g] = 0.f;
+    if constexpr (QREG) {  // each chunk of 16 codes converted once, dotted with every head
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+      for (int i = 0; i < NI; ++i) {
+        float kf[16];
+        fp8x16_to_f32(tl.k[i][0], kf);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d = fmaf(qf[g][e], kf[e], d);
+          s[i][g] = d;
+        }
+      }
+    } else if constexpr (FP8) {  // query from LDS, one head at a time
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const uint4 q0 = qs[((g * CPL) * LPR + c) * QW];
+        const uint4 q1 = qs[((g * CPL) * LPR + c) * QW + 1];
+        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        float qg[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qg[2 * e] = bf16_lo(qw[e]);
+          qg[2 * e + 1] = bf16_hi(qw[e]);
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float kf[16];
+          fp8x16_to_f32(tl.k[i][0], kf);
+          float d = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d = fmaf(qg[e], kf[e], d);
+          s[i][g] = d;
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G && !FP8; ++g) {
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
-        if constexpr (FP8) {  // 16 bf16 query values against 16 e4m3 codes
-          const uint4 q0 = qs[((g * CPL + k) * LPR + c) * QW];
-          const uint4 q1 = qs[((g * CPL + k) * LPR + c) * QW + 1];
-          const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-          float qf[16];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            qf[2 * e] = bf16_lo(qw[e]);
-            qf[2 * e + 1] = bf16_hi(qw[e]);
-          }
-#pragma unroll
-          for (int i = 0; i < NI; ++i) {
-            float kf[16];
-            fp8x16_to_f32(tl.k[i][k], kf);
-            float d = s[i][g];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) d = fmaf(qf[e], kf[e], d);
-            s[i][g] = d;
-          }
-          continue;
-        }
         const uint4 qv = qs[(g * CPL + k) * LPR + c];
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
