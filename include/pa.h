@@ -164,6 +164,26 @@ pa_status pa_decode_fp8(const pa_kv_layout* layout, void* out, const void* q,
                         int32_t num_q_heads, float scale, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Block swap between two pools ("LLM 推理引擎的内存管理与调度" §9 and
+ * "19.2 KV Cache 系统化管理" §19.2.6: a preempted request's KV blocks move to
+ * CPU memory and come back when HBM has room).  For every pair i,
+ * dst_pool[dst_i] = src_pool[src_i], K and V, whole blocks.
+ *   dst_layout : shape and dtype of the destination pools; the source pools
+ *                have the same block shape and dtype and src_num_blocks
+ *                blocks
+ *   dst_k/dst_v, src_k/src_v : device memory or pinned host memory (e.g.
+ *                hipHostMalloc), which the GPU accesses through the same
+ *                pointers: swap-out has host destinations, swap-in host
+ *                sources; the copy runs on the GPU and is bound by the host
+ *                link
+ *   pairs      : int32 [num_pairs, 2] as (src, dst), device or pinned host
+ *                memory; pairs with an id out of range are skipped
+ * Destinations must be distinct.  For fp8 pools swap the scale pools too,
+ * with the same pairs and a layout of head_dim 1 and dtype PA_F32. */
+pa_status pa_swap_blocks(const pa_kv_layout* dst_layout, void* dst_k, void* dst_v,
+                         const void* src_k, const void* src_v, int32_t src_num_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
 /* Copy-on-write of fp8 pools: as pa_copy_blocks, for the codes and the
  * scales of every (src, dst) pair. */
 pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,

@@ -23,7 +23,8 @@ Modules:
 
 * :mod:`oracle.allocator` -- block pool mirror: LIFO free list, reference
   counts, fork, append with copy-on-write, release, block tables.
-* :mod:`oracle.kvcache` -- slot-mapped cache writes and whole-block copies.
+* :mod:`oracle.kvcache` -- slot-mapped cache writes, whole-block copies and
+  block swaps between two pools.
 * :mod:`oracle.attention` -- attention through the block table (the plain
   definition), split-sequence partials and their log-sum-exp merge.
 * :mod:`oracle.quant` -- the e4m3 (FP8) code table and per-token absmax
@@ -34,7 +35,7 @@ each module's docstring and exercised by ``tests/test_oracle_*.py``.
 """
 
 from .allocator import OracleBlockPool, OracleNoFreeBlocks  # noqa: F401
-from .kvcache import kv_write, copy_blocks  # noqa: F401
+from .kvcache import kv_write, copy_blocks, swap_blocks  # noqa: F401
 from .quant import e4m3_decode, e4m3_encode, quantize_rows, dequantize, kv_write_fp8  # noqa: F401
 from .attention import (  # noqa: F401
     bf16_bits_to_f64,

@@ -11,7 +11,11 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
   page: the new block receives the content of the shared one, keys and
   values alike.
 
-Both are bit copies: they work on arrays of any dtype (bf16 pools are held
+* ``swap_blocks`` is the swap of a preempted request ("LLM 推理引擎的内存管理与
+  调度" §9; "19.2 KV Cache 系统化管理" §19.2.6): its blocks move between the
+  device pools and pools in CPU memory, ``dst[d] = src[s]`` for each pair.
+
+All are bit copies: they work on arrays of any dtype (bf16 pools are held
 as their uint16 bit patterns), so results can be compared bit for bit.
 Pins: closed form (a copy), checked elementwise in the tests, plus the
 structural guarantee that the allocator never hands out overlapping pairs.
@@ -46,3 +50,15 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs) -> None:
     for src, dst in pairs:
         k_pool[dst] = k_pool[src]
         v_pool[dst] = v_pool[src]
+
+
+def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray,
+                pairs) -> None:
+    """In place: ``dst[d] = src[s]`` for every ``(s, d)`` pair (two different pools)."""
+    pairs = [(int(s), int(d)) for s, d in pairs]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("swap destinations must be distinct")
+    for src, dst in pairs:
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]

@@ -61,6 +61,7 @@ _SIGNATURES = {
     "pa_decode_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                              _p, ctypes.c_size_t, _p]),
     "pa_copy_blocks_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p]),
+    "pa_swap_blocks": (_i32, [_LAYOUT, _p, _p, _p, _p, _i32, _p, _i32, _p]),
     "pa_decode_split": (_i32, [_LAYOUT, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p,
                                _i32, _i32, _f32, _p]),
     "pa_reduce": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]),
@@ -198,6 +199,40 @@ def kv_write_fp8(k_pool, v_pool, k_scale, v_scale, k_new, v_new, slot_mapping) -
                                  _dev(k_new, "k_new", torch.bfloat16),
                                  _dev(v_new, "v_new", torch.bfloat16),
                                  _dev(slot_mapping, "slot_mapping", torch.int32), n, _stream()))
+
+
+def _host_or_dev(t: torch.Tensor, name: str) -> ctypes.c_void_p:
+    """Device tensor, or pinned host tensor (the GPU reaches it through the same pointer)."""
+    if not isinstance(t, torch.Tensor) or not (t.is_cuda or t.is_pinned()):
+        raise TypeError(f"{name} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs) -> None:
+    """``pa_swap_blocks``: ``dst[d] = src[s]`` for every (s, d) row of ``pairs``.
+
+    Pools are ``[num_blocks, ...block shape]`` device or pinned host tensors of one
+    dtype and block shape (swap-out: host destinations; swap-in: host sources);
+    a pool of any block shape works (fp8 scale pools included).
+    """
+    if dst_k.shape != dst_v.shape or src_k.shape != src_v.shape:
+        raise ValueError("K and V pools must have the same shape")
+    if dst_k.shape[1:] != src_k.shape[1:] or dst_k.dtype != src_k.dtype:
+        raise ValueError("source and destination pools must share block shape and dtype")
+    if pairs.dim() != 2 or pairs.shape[1] != 2 or pairs.dtype != torch.int32:
+        raise ValueError("pairs must be int32 [n, 2]")
+    per_block = int(np.prod(dst_k.shape[1:])) if dst_k.dim() > 1 else 1
+    dt = _DTYPES.get(dst_k.dtype)
+    if dt is None:
+        raise TypeError(f"unsupported pool dtype {dst_k.dtype}")
+    # the block as rows of one element: only its byte size matters to the copy
+    lay = KVLayout(int(dst_k.shape[0]), 1, 1, per_block, dt)
+    _check(lib().pa_swap_blocks(ctypes.byref(lay), _host_or_dev(dst_k, "dst_k"),
+                                _host_or_dev(dst_v, "dst_v"), _host_or_dev(src_k, "src_k"),
+                                _host_or_dev(src_v, "src_v"), int(src_k.shape[0]),
+                                _host_or_dev(pairs, "pairs"), int(pairs.shape[0]), _stream()))
 
 
 def copy_blocks_fp8(k_pool, v_pool, k_scale, v_scale, pairs) -> None:

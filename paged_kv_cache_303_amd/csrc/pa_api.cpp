@@ -309,6 +309,34 @@ pa_status pa_kv_write_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool
                            what);
 }
 
+pa_status pa_swap_blocks(const pa_kv_layout* dst_layout, void* dst_k, void* dst_v,
+                         const void* src_k, const void* src_v, int32_t src_num_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+  const char* what = "pa_swap_blocks";
+  // any block shape (the scale pools of fp8 caches have head_dim 1)
+  if (!dst_layout) return fail(PA_ERR_INVALID_ARG, "%s: layout is NULL", what);
+  if (dst_layout->num_blocks <= 0 || dst_layout->block_size <= 0 ||
+      dst_layout->num_kv_heads <= 0 || dst_layout->head_dim <= 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout sizes must be positive", what);
+  if (dst_layout->dtype != PA_F32 && dst_layout->dtype != PA_BF16 && dst_layout->dtype != PA_FP8)
+    return fail(PA_ERR_UNSUPPORTED, "%s: unknown dtype %d", what, dst_layout->dtype);
+  if ((int64_t)dst_layout->block_size * dst_layout->num_kv_heads * dst_layout->head_dim *
+          pa::elt_bytes(dst_layout->dtype) % 16 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: a block must be a multiple of 16 bytes", what);
+  if (src_num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "%s: src_num_blocks must be > 0", what);
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs)
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  const int64_t block_bytes = (int64_t)dst_layout->block_size * dst_layout->num_kv_heads *
+                              dst_layout->head_dim * pa::elt_bytes(dst_layout->dtype);
+  if ((int64_t)num_pairs * ((block_bytes + 16383) / 16384) > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: too many pairs for one launch", what);
+  return pa::launch_status(pa::launch_swap_blocks(*dst_layout, dst_k, dst_v, src_k, src_v,
+                                                  src_num_blocks, pairs, num_pairs, stream),
+                           what);
+}
+
 pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_pool,
                              float* k_scale, float* v_scale, const int32_t* pairs,
                              int32_t num_pairs, void* stream) {

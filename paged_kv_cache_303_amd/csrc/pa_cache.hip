@@ -167,6 +167,35 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
     a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
 }
 
+// Block copies between two pools (swap out to / in from pinned host memory,
+// which the GPU reads and writes through the same pointers; preemption in
+// "LLM 推理引擎的内存管理与调度" §9 and "19.2 KV Cache 系统化管理" §19.2.6):
+// dst_pool[pair.dst] = src_pool[pair.src], K and V, 16 KiB chunks per
+// workgroup; pairs with an id out of range are skipped.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(
+    char* __restrict__ dk, char* __restrict__ dv, const char* __restrict__ sk,
+    const char* __restrict__ sv, const int32_t* __restrict__ pairs, int64_t block_bytes,
+    int32_t dst_blocks, int32_t src_blocks, int64_t chunks_per_block) {
+  const int64_t pair = blockIdx.x / chunks_per_block;
+  const int64_t chunk = blockIdx.x % chunks_per_block;
+  const int32_t src = pairs[2 * pair];
+  const int32_t dst = pairs[2 * pair + 1];
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const int64_t lo = chunk * kCopyChunk;
+  const int64_t hi = min(lo + kCopyChunk, block_bytes);
+  const int64_t n16 = (hi - lo) >> 4;
+  const uint4* a = (const uint4*)(sk + src * block_bytes + lo);
+  const uint4* b = (const uint4*)(sv + src * block_bytes + lo);
+  uint4* c = (uint4*)(dk + dst * block_bytes + lo);
+  uint4* d = (uint4*)(dv + dst * block_bytes + lo);
+  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
+    const uint4 x = a[i];
+    const uint4 y = b[i];
+    c[i] = x;
+    d[i] = y;
+  }
+}
+
 inline int64_t elt_size(int32_t dtype) {
   return dtype == PA_BF16 ? 2 : (dtype == PA_FP8 ? 1 : 4);
 }
@@ -195,6 +224,19 @@ pa_status launch_kv_write_fp8(const pa_kv_layout& l, void* k_pool, void* v_pool,
                      (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool, k_scale, v_scale,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, slots, l.num_kv_heads,
                      l.head_dim, num_rows);
+  return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status launch_swap_blocks(const pa_kv_layout& l, void* dst_k, void* dst_v, const void* src_k,
+                             const void* src_v, int32_t src_num_blocks, const int32_t* pairs,
+                             int32_t num_pairs, void* stream) {
+  if (num_pairs == 0) return PA_OK;
+  const int64_t block_bytes =
+      (int64_t)l.block_size * l.num_kv_heads * l.head_dim * elt_size(l.dtype);
+  const int64_t chunks = (block_bytes + kCopyChunk - 1) / kCopyChunk;
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3((uint32_t)(num_pairs * chunks)), dim3(256), 0,
+                     (hipStream_t)stream, (char*)dst_k, (char*)dst_v, (const char*)src_k,
+                     (const char*)src_v, pairs, block_bytes, l.num_blocks, src_num_blocks, chunks);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -86,6 +86,11 @@ pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, con
 pa_status launch_kv_write_fp8(const pa_kv_layout& l, void* k_pool, void* v_pool, float* k_scale,
                               float* v_scale, const void* k_new, const void* v_new,
                               const int32_t* slots, int32_t num_tokens, void* stream);
+// dst_pool[dst] = src_pool[src] between two pools of the same layout (one may be
+// pinned host memory); l.num_blocks is the destination's block count.
+pa_status launch_swap_blocks(const pa_kv_layout& l, void* dst_k, void* dst_v, const void* src_k,
+                             const void* src_v, int32_t src_num_blocks, const int32_t* pairs,
+                             int32_t num_pairs, void* stream);
 pa_status launch_copy_blocks(const pa_kv_layout& l, void* k_pool, void* v_pool,
                              const int32_t* pairs, int32_t num_pairs, void* stream);
 
