@@ -60,10 +60,12 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM bytes per launch measured with rocprofv3 counters")
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--workload", choices=["gqa_decode", "long_context"], default="gqa_decode",
+    ap.add_argument("--workload", choices=["gqa_decode", "long_context", "bs_sweep"],
+                    default="gqa_decode",
                     help="gqa_decode: the headline measurement (default); long_context: time "
                          "the mixed split launch (8 x 32K decode + a 512-token causal chunk) "
-                         "and its reduce, for profiling")
+                         "and its reduce, for profiling; bs_sweep: the headline batch at block "
+                         "sizes 8, 16, 32 and 64 (decode time and tail-block waste)")
     return ap.parse_args()
 
 
@@ -86,6 +88,9 @@ def main():
         pa_build.build()
     if args.workload == "long_context":
         _long_context(args)
+        return
+    if args.workload == "bs_sweep":
+        _bs_sweep(args)
         return
     from paged_kv_cache_303_amd import binding, runner, workloads as wl
 
@@ -264,6 +269,46 @@ def _fp8_decode(binding, runner, w, st, new_slots, q, bt_d, sl_d, args, dev):
                               / HBM_PEAK_GBPS, 2),
         "queries_per_s": round(len(w.seq_lens) / (ms * 1e-3), 1),
     }
+
+
+def _bs_sweep(args):
+    """The GQA batch at several block sizes: balanced decode time, effective KV GB/s, and
+    the pool slots lost to partly filled tail blocks ("LLM 推理引擎的内存管理与调度" §3.1
+    on the block-size trade-off)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_303_amd import binding, runner, workloads as wl
+
+    dev = torch.device("cuda", 0)
+    rows = []
+    for bs in (8, 16, 32, 64):
+        w = wl.gqa_decode(seed=args.seed, block_size=bs, num_blocks=65536 * 16 // bs)
+        st = runner.replay(w, dev, poison=False)
+        ws = binding.decode_workspace(st["k_pool"], len(w.seq_lens), w.num_q_heads)
+        out = torch.empty_like(st["q"])
+        call = (st["q"], st["k_pool"], st["v_pool"], st["block_tables"], st["seq_lens"], w.scale)
+        for _ in range(args.warmup):
+            binding.decode(*call, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            binding.decode(*call, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        lens = np.asarray(w.seq_lens, np.int64)
+        slots = int((-(-lens // bs) * bs).sum())
+        rows.append({"block_size": bs, "decode_ms": round(ms, 4),
+                     "kv_GBps": round(w.kv_bytes / (ms * 1e-3) / 1e9, 1),
+                     "pct_hbm_peak": round(100 * w.kv_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                     "tail_waste_pct": round(100.0 * (slots - int(lens.sum())) / slots, 3)})
+        log(f"block size {bs}: {rows[-1]}")
+        del st, ws, out
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": "bs_sweep: gqa_decode batch 256 (32/8 heads, head_dim 128, "
+                                  "bf16, lognormal lengths) at block sizes 8..64",
+                      "steps": args.steps, "rows": rows}), flush=True)
 
 
 def _long_context(args):
