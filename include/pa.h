@@ -276,6 +276,32 @@ pa_status pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens,
  * count reaches 0 is appended to the free list) and forget the sequence. */
 pa_status pa_seq_release(pa_pool* pool, int32_t seq);
 pa_status pa_seq_len(const pa_pool* pool, int32_t seq, int32_t* len);
+
+/* Prefix cache over the pool ("LLM 推理引擎的内存管理与调度" §5.1-5.2, "19.2 KV
+ * Cache 系统化管理" §19.2.5).  A full block is keyed by a chained hash of its
+ * parent's key and its own tokens; a request whose prompt starts with
+ * published blocks reuses them (one more reference each) and skips their
+ * prefill.  Published blocks outlive their requests: at reference count 0
+ * they are evictable rather than free, and an allocation that finds the free
+ * list empty reclaims the least recently released one (blocks released by
+ * one call in logical order).  pa_pool_num_free counts free plus evictable
+ * blocks; pa_pool_free_list lists the free ones only.
+ *
+ * Key of one block: 64-bit FNV-1a (offset basis 0xCBF29CE484222325, prime
+ * 0x100000001B3) over `parent` (8 bytes little endian; 0 for a request's
+ * first block), `salt` (8 bytes little endian: model, adapter or other
+ * context that changes the KV) and the n token ids (4 bytes little endian
+ * each). */
+uint64_t pa_prefix_hash(uint64_t parent, const int32_t* tokens, int32_t n, uint64_t salt);
+/* For an empty sequence: map the cached blocks of keys[0], keys[1], ... in
+ * order until the first key that is not cached; *n_hit blocks are mapped and
+ * the sequence then holds n_hit * block_size tokens. */
+pa_status pa_seq_match_prefix(pa_pool* pool, int32_t seq, const uint64_t* keys, int32_t n,
+                              int32_t* n_hit);
+/* Publish the sequence's first n blocks (all full) under keys[0..n-1].  A key
+ * that another block already holds keeps that block; a block already
+ * published under a different key is an error (nothing changes). */
+pa_status pa_seq_register_prefix(pa_pool* pool, int32_t seq, const uint64_t* keys, int32_t n);
 /* Host int32 out[n, max_blocks]: row i = table of seqs[i], padded with fill. */
 pa_status pa_block_tables(const pa_pool* pool, const int32_t* seqs, int32_t n,
                           int32_t max_blocks, int32_t fill, int32_t* out);

@@ -35,6 +35,19 @@ Readings taken where the pages are silent (each is listed in the design doc):
   ``(old, new)`` is returned so that the device copy can run before the
   device write.
 
+Prefix cache ("LLM 推理引擎的内存管理与调度" §5.1-5.2; "19.2 KV Cache 系统化管理"
+§19.2.5): a full block is keyed by a chained hash ``h_i = H(h_{i-1},
+tokens_i, extra)``; a new request looks its prompt's keys up block by block,
+and every hit maps the cached block into its table with one more reference
+(the prefill of that block is skipped); the first miss ends the match.
+Cached blocks survive their requests: at reference count zero they become
+evictable instead of free, and are reclaimed least recently released first
+when the free list is empty.  Readings: H is 64-bit FNV-1a over the parent
+key, a salt (the page's model / adapter / extra fields) and the token ids
+(byte order below); the first block's parent key is 0; blocks released by
+one call enter the eviction order in logical order; registering a key that
+another block already holds keeps the first block.
+
 Pins: the pages' worked example (10 tokens, block size 4, 16 blocks ->
 blocks [15, 14, 13], 16/16 free after release), the lifecycle example of
 §19.2.2 (7-token prompt in blocks 7 and 1, the 9th token opens block 3),
@@ -44,6 +57,28 @@ releasing everything -- checked by brute force against a set-based model.
 """
 
 from __future__ import annotations
+
+from collections import OrderedDict
+
+FNV64_OFFSET = 0xCBF29CE484222325
+FNV64_PRIME = 0x100000001B3
+
+
+def fnv1a64(data: bytes, h: int = FNV64_OFFSET) -> int:
+    """64-bit FNV-1a: for every byte, xor it in, then multiply by the FNV prime."""
+    for byte in data:
+        h ^= byte
+        h = (h * FNV64_PRIME) & 0xFFFFFFFFFFFFFFFF
+    return h
+
+
+def prefix_hash(parent: int, tokens, salt: int = 0) -> int:
+    """Key of one full block: FNV-1a over the parent key (8 bytes, little
+    endian), the salt (8 bytes, little endian) and every token id (4 bytes,
+    little endian, two's complement)."""
+    data = int(parent).to_bytes(8, "little") + int(salt).to_bytes(8, "little")
+    data += b"".join((int(t) & 0xFFFFFFFF).to_bytes(4, "little") for t in tokens)
+    return fnv1a64(data)
 
 
 class OracleNoFreeBlocks(RuntimeError):
@@ -65,22 +100,73 @@ class OracleBlockPool:
             if sorted(self.free_list) != list(range(self.num_blocks)):
                 raise ValueError("initial_free must be a permutation of the block ids")
         self.ref_counts = [0] * self.num_blocks
+        # prefix cache: key -> block, block -> key, evictable blocks (oldest first)
+        self.cached: dict[int, int] = {}
+        self.block_key: dict[int, int] = {}
+        self.evictable: OrderedDict[int, None] = OrderedDict()
         # seq id -> [mapping(list of physical ids), num_filled]
         self.seqs: dict[int, list] = {}
         self._next_seq = 0
 
     # -- PhysicalBlockPool.allocate / release --------------------------------
     def _allocate(self) -> int:
-        if not self.free_list:
+        if self.free_list:
+            block = self.free_list.pop()
+        elif self.evictable:  # reclaim the least recently released cached block
+            block, _ = self.evictable.popitem(last=False)
+            del self.cached[self.block_key.pop(block)]
+        else:
             raise OracleNoFreeBlocks("no free physical block")
-        block = self.free_list.pop()
         self.ref_counts[block] = 1
         return block
 
     def _release_block(self, block: int) -> None:
         self.ref_counts[block] -= 1
         if self.ref_counts[block] == 0:
-            self.free_list.append(block)
+            if block in self.block_key:
+                self.evictable[block] = None
+            else:
+                self.free_list.append(block)
+
+    def available(self) -> int:
+        """Blocks an allocation can take: free ones and evictable cached ones."""
+        return len(self.free_list) + len(self.evictable)
+
+    # -- prefix cache --------------------------------------------------------
+    def match_prefix(self, seq: int, keys) -> int:
+        """Map the cached blocks of the longest matching key chain into the
+        empty request ``seq``; returns the number of blocks hit."""
+        mapping, filled = self.seqs[seq]
+        if mapping or filled:
+            raise ValueError("match_prefix needs an empty sequence")
+        hits = 0
+        for key in keys:
+            block = self.cached.get(int(key))
+            if block is None:
+                break
+            if self.ref_counts[block] == 0:
+                del self.evictable[block]
+            self.ref_counts[block] += 1
+            mapping.append(block)
+            hits += 1
+        self.seqs[seq][1] = hits * self.block_size
+        return hits
+
+    def register_prefix(self, seq: int, keys) -> None:
+        """Publish the first ``len(keys)`` (full) blocks of ``seq`` under ``keys``."""
+        mapping, filled = self.seqs[seq]
+        if len(keys) > filled // self.block_size:
+            raise ValueError("only full blocks can be registered")
+        for i, key in enumerate(keys):
+            key, block = int(key), mapping[i]
+            if block in self.block_key:
+                if self.block_key[block] != key:
+                    raise ValueError("block already cached under another key")
+                continue
+            if key in self.cached:
+                continue  # another block holds this prefix already: the first one stays
+            self.cached[key] = block
+            self.block_key[block] = key
 
     # -- request lifecycle ---------------------------------------------------
     def new_seq(self) -> int:
@@ -122,7 +208,7 @@ class OracleBlockPool:
         """
         if n_tokens < 0:
             raise ValueError("n_tokens must be >= 0")
-        if self.blocks_needed(seq, n_tokens) > len(self.free_list):
+        if self.blocks_needed(seq, n_tokens) > self.available():
             raise OracleNoFreeBlocks("not enough free blocks for append")
         state = self.seqs[seq]
         mapping = state[0]
@@ -159,7 +245,8 @@ class OracleBlockPool:
         return list(self.seqs[seq][0])
 
     def num_free(self) -> int:
-        return len(self.free_list)
+        """Free plus evictable blocks (what allocations can still take)."""
+        return self.available()
 
     def block_tables(self, seqs, max_blocks: int, fill: int = -1):
         """Rows of physical ids, one per sequence, padded with ``fill``."""

@@ -77,6 +77,9 @@ _SIGNATURES = {
     "pa_seq_release": (_i32, [_p, _i32]),
     "pa_seq_len": (_i32, [_p, _i32, _pi32]),
     "pa_block_tables": (_i32, [_p, _pi32, _i32, _i32, _i32, _pi32]),
+    "pa_prefix_hash": (ctypes.c_uint64, [ctypes.c_uint64, _pi32, _i32, ctypes.c_uint64]),
+    "pa_seq_match_prefix": (_i32, [_p, _i32, ctypes.POINTER(ctypes.c_uint64), _i32, _pi32]),
+    "pa_seq_register_prefix": (_i32, [_p, _i32, ctypes.POINTER(ctypes.c_uint64), _i32]),
 }
 
 _LIB = None
@@ -389,6 +392,13 @@ def _ptr32(a: np.ndarray):
     return a.ctypes.data_as(_pi32)
 
 
+def prefix_hash(parent: int, tokens, salt: int = 0) -> int:
+    """``pa_prefix_hash``: the chained key of one full block."""
+    t = _i32_array(tokens)
+    return int(lib().pa_prefix_hash(ctypes.c_uint64(int(parent)), _ptr32(t), int(t.shape[0]),
+                                    ctypes.c_uint64(int(salt))))
+
+
 class BlockPool:
     """The library's host block pool (free list, reference counts, tables)."""
 
@@ -436,6 +446,22 @@ class BlockPool:
         s = ctypes.c_int32()
         _check(lib().pa_seq_fork(self._h, int(parent), ctypes.byref(s)))
         return s.value
+
+    def match_prefix(self, seq: int, keys) -> int:
+        """``pa_seq_match_prefix``: map cached blocks of the key chain; returns the hits."""
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        n = ctypes.c_int32()
+        _check(lib().pa_seq_match_prefix(self._h, int(seq),
+                                         k.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                         int(k.shape[0]), ctypes.byref(n)))
+        return n.value
+
+    def register_prefix(self, seq: int, keys) -> None:
+        """``pa_seq_register_prefix``: publish the sequence's first full blocks."""
+        k = np.ascontiguousarray(np.asarray(keys, dtype=np.uint64))
+        _check(lib().pa_seq_register_prefix(self._h, int(seq),
+                                            k.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                            int(k.shape[0])))
 
     def blocks_needed(self, seq: int, n_tokens: int) -> int:
         n = ctypes.c_int32()

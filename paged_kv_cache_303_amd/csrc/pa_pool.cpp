@@ -11,11 +11,20 @@
 // count; the first write into a shared, partly filled block copies it to a
 // new block, remaps the table and lowers the old count).
 //
+// Prefix cache ("LLM 推理引擎的内存管理与调度" §5.1-5.2; "19.2 KV Cache
+// 系统化管理" §19.2.5): full blocks can be published under a chained key
+// h_i = H(h_{i-1}, tokens_i, salt) (pa_prefix_hash: 64-bit FNV-1a); a new
+// request maps the longest chain of published keys into its table, one more
+// reference per hit; a published block whose count drops to zero becomes
+// evictable instead of free, and allocation reclaims the least recently
+// released evictable block once the free list is empty.
+//
 // All operations are O(1) per token or block and all-or-nothing: every
 // failure is detected before the pool is touched.
 
 #include <cstdint>
 #include <cstring>
+#include <list>
 #include <new>
 #include <string>
 #include <unordered_map>
@@ -35,15 +44,38 @@ struct pa_pool {
   };
   std::unordered_map<int32_t, Seq> seqs;
   int32_t next_seq = 0;
+  // prefix cache: key -> block; per block its key; evictable blocks, oldest first
+  std::unordered_map<uint64_t, int32_t> cached;
+  std::vector<uint64_t> key_of;
+  std::vector<char> has_key;
+  std::list<int32_t> evictable;
+  std::vector<std::list<int32_t>::iterator> evict_pos;
 
+  int64_t available() const { return (int64_t)free_list.size() + (int64_t)evictable.size(); }
+
+  // Caller checked available() > 0.
   int32_t take() {
-    int32_t b = free_list.back();
-    free_list.pop_back();
+    int32_t b;
+    if (!free_list.empty()) {
+      b = free_list.back();
+      free_list.pop_back();
+    } else {  // reclaim the least recently released cached block
+      b = evictable.front();
+      evictable.pop_front();
+      cached.erase(key_of[b]);
+      has_key[b] = 0;
+    }
     refcount[b] = 1;
     return b;
   }
   void drop(int32_t b) {
-    if (--refcount[b] == 0) free_list.push_back(b);
+    if (--refcount[b] > 0) return;
+    if (has_key[b]) {
+      evictable.push_back(b);
+      evict_pos[b] = std::prev(evictable.end());
+    } else {
+      free_list.push_back(b);
+    }
   }
   // Blocks an append of n tokens would take (copy-on-write + new blocks).
   int64_t needed(const Seq& s, int64_t n) const {
@@ -84,6 +116,9 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
   p->num_blocks = num_blocks;
   p->block_size = block_size;
   p->refcount.assign(num_blocks, 0);
+  p->key_of.assign(num_blocks, 0);
+  p->has_key.assign(num_blocks, 0);
+  p->evict_pos.resize(num_blocks);
   p->free_list.resize(num_blocks);
   if (initial_free) {
     std::vector<char> seen(num_blocks, 0);
@@ -107,7 +142,7 @@ pa_status pa_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* 
 void pa_pool_destroy(pa_pool* pool) { delete pool; }
 
 int32_t pa_pool_num_free(const pa_pool* pool) {
-  return pool ? (int32_t)pool->free_list.size() : -1;
+  return pool ? (int32_t)pool->available() : -1;
 }
 
 int32_t pa_pool_refcount(const pa_pool* pool, int32_t block) {
@@ -168,7 +203,7 @@ pa_status pa_seq_append(pa_pool* pool, int32_t seq, int32_t n_tokens, int32_t* s
       (int64_t)pool->num_blocks * bs > (int64_t)INT32_MAX + 1)
     return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_append: slot index would overflow int32");
   const int64_t need = pool->needed(*s, n_tokens);
-  if (need > (int64_t)pool->free_list.size())
+  if (need > pool->available())
     return pa::fail(PA_ERR_NO_FREE_BLOCKS, "pa_seq_append: not enough free blocks");
   // At most the first token can land in a shared block (later ones see a
   // private block), so one pair of room is enough.
@@ -204,6 +239,70 @@ pa_status pa_seq_release(pa_pool* pool, int32_t seq) {
   if (it == pool->seqs.end()) return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_release: unknown sequence");
   for (int32_t b : it->second.blocks) pool->drop(b);
   pool->seqs.erase(it);
+  return PA_OK;
+}
+
+uint64_t pa_prefix_hash(uint64_t parent, const int32_t* tokens, int32_t n, uint64_t salt) {
+  // 64-bit FNV-1a over parent (8 bytes LE), salt (8 bytes LE), token ids (4 bytes LE)
+  uint64_t h = 0xCBF29CE484222325ull;
+  auto eat = [&](uint64_t v, int bytes) {
+    for (int i = 0; i < bytes; ++i) {
+      h ^= (v >> (8 * i)) & 0xFFu;
+      h *= 0x100000001B3ull;
+    }
+  };
+  eat(parent, 8);
+  eat(salt, 8);
+  for (int32_t i = 0; tokens && i < n; ++i) eat((uint32_t)tokens[i], 4);
+  return h;
+}
+
+pa_status pa_seq_match_prefix(pa_pool* pool, int32_t seq, const uint64_t* keys, int32_t n,
+                              int32_t* n_hit) {
+  if (!pool || !n_hit || (n > 0 && !keys))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_match_prefix: NULL argument");
+  if (n < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_match_prefix: n < 0");
+  pa_pool::Seq* s = find(pool, seq);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_match_prefix: unknown sequence");
+  if (s->filled != 0 || !s->blocks.empty())
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_match_prefix: the sequence is not empty");
+  if ((int64_t)n * pool->block_size > (int64_t)INT32_MAX)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_match_prefix: too many blocks");
+  int32_t hits = 0;
+  for (; hits < n; ++hits) {
+    auto it = pool->cached.find(keys[hits]);
+    if (it == pool->cached.end()) break;
+    const int32_t b = it->second;
+    if (pool->refcount[b] == 0) pool->evictable.erase(pool->evict_pos[b]);
+    pool->refcount[b] += 1;
+    s->blocks.push_back(b);
+  }
+  s->filled = (int64_t)hits * pool->block_size;
+  *n_hit = hits;
+  return PA_OK;
+}
+
+pa_status pa_seq_register_prefix(pa_pool* pool, int32_t seq, const uint64_t* keys, int32_t n) {
+  if (!pool || (n > 0 && !keys))
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_register_prefix: NULL argument");
+  if (n < 0) return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_register_prefix: n < 0");
+  pa_pool::Seq* s = find(pool, seq);
+  if (!s) return pa::fail(PA_ERR_NOT_FOUND, "pa_seq_register_prefix: unknown sequence");
+  if (n > s->filled / pool->block_size)
+    return pa::fail(PA_ERR_INVALID_ARG, "pa_seq_register_prefix: only full blocks can be registered");
+  for (int32_t i = 0; i < n; ++i) {  // check first: all-or-nothing
+    const int32_t b = s->blocks[i];
+    if (pool->has_key[b] && pool->key_of[b] != keys[i])
+      return pa::fail(PA_ERR_INVALID_ARG,
+                      "pa_seq_register_prefix: block %d is already cached under another key", b);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t b = s->blocks[i];
+    if (pool->has_key[b] || pool->cached.count(keys[i])) continue;  // first holder stays
+    pool->cached.emplace(keys[i], b);
+    pool->key_of[b] = keys[i];
+    pool->has_key[b] = 1;
+  }
   return PA_OK;
 }
 
