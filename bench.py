@@ -147,7 +147,8 @@ def main():
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_step = 1e3 * t_total / args.steps
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    per_call = np.array([a.elapsed_time(b) for a, b in events])
+    decode_ms = float(per_call.mean())
 
     # the fixed-partition path (split + reduce), for context
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -203,6 +204,9 @@ def main():
         "queries_per_s": round(len(seq_lens) / (ms_step * 1e-3), 1),
         "decode_only": {
             "ms": round(decode_ms, 4),
+            "p10_ms": round(float(np.percentile(per_call, 10)), 4),
+            "p50_ms": round(float(np.percentile(per_call, 50)), 4),
+            "p90_ms": round(float(np.percentile(per_call, 90)), 4),
             "kv_GBps": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 1),
             "queries_per_s": round(len(seq_lens) / (decode_ms * 1e-3), 1),
         },
