@@ -73,10 +73,6 @@ pa_status check_heads(const pa_kv_layout* l, int32_t num_q_heads, const char* wh
   return PA_OK;
 }
 
-#ifndef PA_WAVES_PER_GROUP
-#define PA_WAVES_PER_GROUP 2
-#endif
-
 // KV heads handled by one workgroup (one wave each): the largest divisor of
 // num_kv_heads that is at most PA_WAVES_PER_GROUP.
 int32_t waves_per_group(int32_t num_kv_heads) {

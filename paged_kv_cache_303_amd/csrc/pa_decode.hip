@@ -84,7 +84,7 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 //        redundant exponentials; 1 when G is large, to bound accumulators)
 //   LPR  lanes per token row, TPI rows per load instruction
 //   NI   load instructions (of CPL chunks each) per tile, TT tokens per tile
-template <typename T, int D, int G, bool UNIFORM = true>
+template <typename T, int D, int G, bool UNIFORM = true, int TILE = 0>
 struct Shape {
   static constexpr int VEC = Elt<T>::kVec;
   static constexpr int CHUNKS = D / VEC;
@@ -98,7 +98,9 @@ struct Shape {
   static constexpr int MAX_LOADS =
       (sizeof(T) <= 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
       : (G >= 8 ? PA_MAX_TILE_LOADS / 4 : PA_MAX_TILE_LOADS / 2);
-  static constexpr int TILE_TOKENS = sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : PA_TILE_TOKENS;
+  // target tokens per tile: TILE if given, else the default of the type
+  static constexpr int TILE_TOKENS =
+      TILE > 0 ? TILE : (sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : PA_TILE_TOKENS);
   static constexpr int NI0 = (TILE_TOKENS / TPI) < 1 ? 1 : (TILE_TOKENS / TPI);
   static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
   static constexpr int TT = NI * TPI;
@@ -120,9 +122,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 // UNIFORM: the rows of one load instruction always share a block (the block
 // size is a multiple of TPI), so block-table entries are wave-uniform scalar
 // loads; otherwise every lane looks its block up.
-template <typename T, int D, int G, bool UNIFORM>
+template <typename T, int D, int G, bool UNIFORM, int TILE = 0>
 struct WaveCtx {
-  using S = Shape<T, D, G, UNIFORM>;
+  using S = Shape<T, D, G, UNIFORM, TILE>;
   static constexpr int VEC = S::VEC, CPL = S::CPL, LPR = S::LPR, LOG_LPR = ilog2(S::LPR);
   static constexpr int TPI = S::TPI, NI = S::NI, TT = S::TT;
   static constexpr bool BF16 = sizeof(T) == 2;
@@ -704,17 +706,17 @@ __device__ __forceinline__ int64_t slice_start(int64_t r, int64_t T, int64_t R) 
 __device__ __forceinline__ int uniform_lds(const int* p) { return __builtin_amdgcn_readfirstlane(*p); }
 
 // Work units of a sequence in the balanced decode's static slicing: its tiles
-// plus kSeqCost units for the pipeline restart at every sequence a slice
-// holds (query load, first block-table lookups and gathers, and the final
-// cross-lane combine and store).  Per-wave timestamps on MI355X put one
-// restart at 5-7 us, two to three tiles' time; a sweep of kSeqCost over
-// 0..6 on the batch-256 GQA decode is fastest at 4 (2% below 0).  The extra
-// units come first: sequence b occupies units [cum[b], cum[b+1]), its tiles
-// are the last tiles(b) of them, and an empty sequence has none.
-#ifndef PA_SEQ_COST
-#define PA_SEQ_COST 4
+// plus the cost of the pipeline restart at every sequence a slice holds
+// (query load, first block-table lookups and gathers, and the final
+// cross-lane combine and store), PA_SEQ_COST_TOKENS tokens' worth of tiles.
+// Per-wave timestamps on MI355X put one restart at 5-7 us; a sweep over 0..6
+// tiles of 16 tokens on the batch-256 GQA decode is fastest at 4 (2% below
+// 0).  The extra units come first: sequence b occupies units
+// [cum[b], cum[b+1]), its tiles are the last tiles(b) of them, and an empty
+// sequence has none.
+#ifndef PA_SEQ_COST_TOKENS
+#define PA_SEQ_COST_TOKENS 64
 #endif
-constexpr int kSeqCost = PA_SEQ_COST;
 
 // Prefix sums of work units per sequence into LDS: ends[b] = len_b (clamped
 // to the table's capacity), cum[b] = units of sequences 0..b-1 (TT tokens a
@@ -722,6 +724,7 @@ constexpr int kSeqCost = PA_SEQ_COST;
 // Ends with a workgroup barrier.
 template <int TT>
 __device__ void tile_prefix(const DecodeArgs& a, int* cum, int* ends) {
+  constexpr int kSeqCost = (PA_SEQ_COST_TOKENS + TT - 1) / TT;
   const int B = a.num_seqs;
   const int cap = a.max_blocks << a.log2_bs;
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -760,12 +763,25 @@ __device__ __forceinline__ int seq_of_tile(const int* cum, int B, int64_t t) {
   return lo;
 }
 
+// The streaming kernel runs workgroups of at most kStreamWaves waves and may
+// take a whole SIMD per wave (its launch bounds allow 512 VGPRs), so its
+// tiles are twice as deep as the grid kernel's for bf16 and fp32: 16 KiB of
+// K/V in flight per wave.  On MI355X one deep wave per SIMD beats two
+// shallow ones that share it, one of which the hardware serves measurably
+// slower (batch-256 GQA decode: 0.2935 -> 0.2880 ms).
+constexpr int kStreamWaves = 2;
+static_assert(PA_WAVES_PER_GROUP <= kStreamWaves, "stream workgroups hold at most 2 waves");
+template <typename T>
+constexpr int stream_tile() {
+  return sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : 2 * PA_TILE_TOKENS;
+}
+
 // block_tables is a separate __restrict__ argument: nothing the kernel stores
 // can alias it, so its wave-uniform lookups stay scalar loads after stores.
 template <typename T, int D, int G, bool UNIFORM>
-__global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
+__global__ __launch_bounds__(kStreamWaves * kWave, 1) void decode_stream_kernel(
     DecodeArgs a, StreamArgs s, const int32_t* __restrict__ block_tables) {
-  using W = WaveCtx<T, D, G, UNIFORM>;
+  using W = WaveCtx<T, D, G, UNIFORM, stream_tile<T>()>;
   constexpr int TT = W::TT;
   extern __shared__ int lds[];
   const int B = a.num_seqs;
@@ -776,6 +792,7 @@ __global__ __launch_bounds__(kMaxWaves * kWave) void decode_stream_kernel(
   const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
 
   tile_prefix<TT>(a, cum, ends);
+  constexpr int kSeqCost = (PA_SEQ_COST_TOKENS + TT - 1) / TT;
   const int64_t total = uniform_lds(&cum[B]);
   // slices actually used: at most one per tile, so none is empty
   const int64_t R = min((int64_t)s.num_slices, total);

@@ -6,6 +6,11 @@
 
 #include "../../include/pa.h"
 
+// KV heads (one wave each) per decode workgroup, at most.
+#ifndef PA_WAVES_PER_GROUP
+#define PA_WAVES_PER_GROUP 2
+#endif
+
 namespace pa {
 
 struct DecodeArgs {
