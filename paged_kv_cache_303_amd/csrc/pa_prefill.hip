@@ -11,10 +11,14 @@
 // part_lse[j][h][p] = ln(sum exp(scale * q.k)) over the partition, which
 // pa_reduce merges like any other query's partitions.
 //
-// Work item: (tile of 64 query rows, partition, KV head) of a sequence with
-// q_len > 1.  A query row is a (token, query head) pair of the G heads
-// sharing the KV head, so rows = q_len * G and 64 rows = 64 / G tokens; each
-// of the 4 waves owns 16 rows.  The workgroups are persistent: each counts
+// Work item: (tile of 16 * kPfWaves query rows, partition, KV head) of a
+// sequence with q_len > 1.  A query row is a (token, query head) pair of the
+// G heads sharing the KV head, so rows = q_len * G, and 128 rows (8 waves)
+// are 128 / G tokens; each wave owns 16 rows.  Every K/V tile gathered into
+// LDS serves all rows of the workgroup, so the row tile sets how often a
+// partition's K/V is re-read: 8 waves read it half as often as 4, and a
+// 512-token chunk after 4096 cached tokens took 104 us instead of 145.  The workgroups are persistent
+// (two per compute unit at 8 waves, all resident): each counts
 // the items of every sequence (prefix sums in LDS) and takes items
 // blockIdx.x, blockIdx.x + gridDim.x, ...; consecutive items are row tiles
 // of one (partition, head), so workgroups running together read the same
@@ -44,8 +48,19 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Staging registers of the K/V gathers.  A native vector type: copies of
+// HIP's struct uint4 between global memory, a local array and LDS are
+// memcpys that stay in private (scratch) memory, whose store makes every
+// prefetch load wait at once.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kPfWaves = 4;             // waves per workgroup
+#ifndef PA_PF_WAVES
+#define PA_PF_WAVES 8
+#endif
+#ifndef PA_PF_BLOCKS_PER_CU
+#define PA_PF_BLOCKS_PER_CU 2
+#endif
+constexpr int kPfWaves = PA_PF_WAVES;   // waves per workgroup (16 query rows each)
 constexpr int kPfRows = 16 * kPfWaves;  // query rows per workgroup
 constexpr int kPfKeys = 32;             // keys per tile (a multiple of 32)
 constexpr int kPad = 8;                 // bf16 elements of padding per LDS row
@@ -53,7 +68,7 @@ constexpr float kLn2Pf = 0.69314718055994530942f;
 constexpr float kPfLazy = 8.0f;  // running-max slack (log2 units) before a rescale
 constexpr int kPrefillMaxSeqs = 1024;   // sequences per launch (LDS prefix sums)
 constexpr int kPfMaxBlocks = 1024;      // block ids of one partition staged in LDS
-constexpr int kPfBlocksPerCu = 3;       // persistent workgroups per compute unit (all resident)
+constexpr int kPfBlocksPerCu = PA_PF_BLOCKS_PER_CU;  // persistent workgroups per compute unit
 
 __device__ __forceinline__ f32x4 mfma(uint4 a, uint4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -187,7 +202,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
     // row.  V: pair-chunk cv = (key pair kp = cv % 16, column dc = cv / 16),
     // both rows of the pair, so that each dim's two values pack into one
     // 32-bit LDS store of the transposed tile.
-    uint4 kreg[NLD], vreg[NLDV][2];
+    u32x4 kreg[NLD], vreg[NLDV][2];
     auto row_off = [&](int key) {
       const int kk = min(key, k_hi - 1);  // keys past the item's range are masked
       const int phys = blk_lds[(kk >> a.log2_bs) - blk0];
@@ -197,14 +212,14 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
 #pragma unroll
       for (int n = 0; n < NLD; ++n) {
         const int ci = min((int)threadIdx.x + n * kPfWaves * kWave, NCH - 1);
-        kreg[n] = *(const uint4*)(kp + row_off(k0 + ci / CPR) + (ci % CPR) * 16);
+        kreg[n] = *(const u32x4*)(kp + row_off(k0 + ci / CPR) + (ci % CPR) * 16);
       }
 #pragma unroll
       for (int n = 0; n < NLDV; ++n) {
         const int cv = min((int)threadIdx.x + n * kPfWaves * kWave, NCHV - 1);
         const int kp2 = 2 * (cv % (kPfKeys / 2)), dc = cv / (kPfKeys / 2);
-        vreg[n][0] = *(const uint4*)(vp + row_off(k0 + kp2) + dc * 16);
-        vreg[n][1] = *(const uint4*)(vp + row_off(k0 + kp2 + 1) + dc * 16);
+        vreg[n][0] = *(const u32x4*)(vp + row_off(k0 + kp2) + dc * 16);
+        vreg[n][1] = *(const u32x4*)(vp + row_off(k0 + kp2 + 1) + dc * 16);
       }
     };
     gather(k_lo);
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void prefill_mfma_kernel(
       for (int n = 0; n < NLD; ++n) {
         const int ci = threadIdx.x + n * kPfWaves * kWave;
         if (NCH % (kPfWaves * kWave) != 0 && ci >= NCH) continue;
-        *(uint4*)(k_lds + (ci / CPR) * KS + (ci % CPR) * 8) = kreg[n];
+        *(u32x4*)(k_lds + (ci / CPR) * KS + (ci % CPR) * 8) = kreg[n];
       }
 #pragma unroll
       for (int n = 0; n < NLDV; ++n) {
