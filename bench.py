@@ -26,8 +26,14 @@ Reported:
   fp8_kv         the same batch decoded from an FP8 (e4m3) cache with
                  per-(token, KV head) scales (pa_kv_write_fp8 + pa_decode_fp8):
                  decode time, effective GB/s of codes + scales, queries/s
-  cpu_baseline   the CPU oracle (float64 NumPy, single thread) timed on a
-                 bounded sample of the same queries (seeded order, ~15 s)
+  mha_decode     the MHA batch (32 sequences, 40 heads, lengths U{128..2048}):
+                 balanced decode time, KV GB/s, % of HBM peak, queries/s
+  long_context   8 x 32768 decode + a 512-token causal prefill chunk in one
+                 split launch + reduce: call time, its split/reduce parts,
+                 GB/s and the fraction of its roofline time
+  cpu_baseline   the CPU oracle (float64 NumPy) timed on a bounded sample of
+                 the same queries (seeded order) on every host core the
+                 process may use, and on one thread
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -53,7 +59,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--partition", type=int, default=512)
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run pa_copy_blocks over this many MiB (counter calibration)")
@@ -118,9 +124,7 @@ def main():
     q = runner.to_device(w.q, w.dtype, dev)
     k_pool, v_pool = st["k_pool"], st["v_pool"]
     maxp = binding.max_partitions_for(w.max_blocks, w.block_size, args.partition)
-    part_o = torch.empty((len(seq_lens), w.num_q_heads, maxp, w.head_dim), dtype=torch.float32,
-                         device=dev)
-    part_lse = torch.empty(part_o.shape[:3], dtype=torch.float32, device=dev)
+    split_ws = binding.SplitWorkspace(len(seq_lens), w.num_q_heads, w.head_dim, maxp, dev)
     out = torch.empty_like(q)
     ws = binding.decode_workspace(k_pool, len(seq_lens), w.num_q_heads)
     torch.cuda.synchronize()
@@ -154,10 +158,8 @@ def main():
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        binding.decode_split(q, k_pool, v_pool, bt_d, sl_d, w.scale,
-                             partition_size=args.partition, part_o=part_o, part_lse=part_lse,
-                             max_partitions=maxp)
-        binding.reduce(part_o, part_lse, sl_d, args.partition, out_dtype=q.dtype, out=out)
+        binding.paged_attention(q, k_pool, v_pool, bt_d, sl_d, w.scale,
+                                partition_size=args.partition, workspace=split_ws, out=out)
     e1.record()
     torch.cuda.synchronize()
     split_ms = e0.elapsed_time(e1) / args.steps
@@ -166,6 +168,10 @@ def main():
 
     if args.calib_copy_mib > 0:
         _calibration_copy(binding, k_pool, v_pool, args.calib_copy_mib, dev)
+    del split_ws, st, k_pool, v_pool
+    torch.cuda.empty_cache()
+    mha = _mha_decode(args)
+    lc = _long_context_metrics(args)
 
     kv_bytes = w.kv_bytes
     esize = 2
@@ -216,6 +222,8 @@ def main():
             "kv_GBps": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1),
         },
         "fp8_kv": fp8,
+        "mha_decode": mha,
+        "long_context": lc,
         "roofline": {
             "kernel": "pa_decode (decode_stream_kernel<bf16,128,4> + stream_fixup_kernel)",
             "bound": "hbm",
@@ -318,27 +326,124 @@ def _bs_sweep(args):
 def _long_context(args):
     """Mixed split launch: 8 decode sequences of 32768 tokens and a causal
     512-token prefill chunk in one pa_decode_split, then pa_reduce."""
+    print(json.dumps(_long_context_metrics(args)), flush=True)
+
+
+def _timed(fn, steps, warmup):
+    """Mean ms per call of fn() from HIP events on torch's current stream."""
     import torch
-    from paged_kv_cache_303_amd import runner, workloads as wl
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _mha_decode(args):
+    """The MHA batch: 32 sequences, 40 heads (MHA), head dim 128, block size 16, bf16,
+    lengths uniform in [128, 2048], 4096-block pool; balanced pa_decode."""
+    import torch
+    from paged_kv_cache_303_amd import binding, runner, workloads as wl
+
+    dev = torch.device("cuda", 0)
+    w = wl.mha_decode()
+    st = runner.replay(w, dev, poison=False)
+    ws = binding.decode_workspace(st["k_pool"], len(w.seq_lens), w.num_q_heads)
+    out = torch.empty_like(st["q"])
+    call = (st["q"], st["k_pool"], st["v_pool"], st["block_tables"], st["seq_lens"], w.scale)
+    ms = _timed(lambda: binding.decode(*call, out=out, workspace=ws), args.steps, args.warmup)
+    n = len(w.seq_lens)
+    alg = w.kv_bytes + 2 * n * w.num_q_heads * w.head_dim * 2 + \
+        4 * sum(-(-x // w.block_size) for x in w.seq_lens)
+    res = {"workload": "mha_decode: batch 32, 40/40 heads, head_dim 128, block_size 16, bf16, "
+                       "lengths U{128..2048}, 4096-block pool, balanced pa_decode",
+           "ms": round(ms, 4), "kv_bytes": int(w.kv_bytes),
+           "kv_GBps": round(w.kv_bytes / (ms * 1e-3) / 1e9, 1),
+           "pct_hbm_peak": round(100 * alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+           "queries_per_s": round(n / (ms * 1e-3), 1)}
+    log(f"mha_decode: {res}")
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def _long_context_metrics(args):
+    """Long context + chunked prefill: 8 decode sequences of 32768 tokens and a
+    causal 512-token chunk after 4096 cached tokens in one pa_decode_split
+    launch, then pa_reduce.  Reported against the call's roofline
+    t_min = max(bytes / HBM peak, flops / bf16 MFMA peak)."""
+    import numpy as np
+    import torch
+    from paged_kv_cache_303_amd import binding, runner, workloads as wl
 
     dev = torch.device("cuda", 0)
     w = wl.long_context()
     st = runner.replay(w, dev, poison=False)
-    for _ in range(args.warmup):
-        runner.attention(w, st)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        runner.attention(w, st)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    print(json.dumps({"workload": "long_context: 8 x 32768 decode + 512-token causal chunk "
-                                  "after 4096 tokens, bs 32, 32/8 heads, d 128, bf16, P 512",
-                      "ms_per_call": round(ms, 4), "steps": args.steps,
-                      "kv_bytes": int(w.kv_bytes),
-                      "kv_GBps": round(w.kv_bytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    ws = runner.split_workspace(w, st)
+    out = torch.empty_like(st["q"])
+    p = w.partition_size
+    call = lambda: runner.attention(w, st, workspace=ws, out=out)
+    split = lambda: binding.decode_split(st["q"], st["k_pool"], st["v_pool"], st["block_tables"],
+                                         st["seq_lens"], w.scale, partition_size=p,
+                                         cu_q_lens=st["cu_q_lens"], workspace=ws)
+    red = lambda: binding.reduce(ws, st["seq_lens"], p, out_dtype=st["q"].dtype,
+                                 cu_q_lens=st["cu_q_lens"], out=out)
+    ms = _timed(call, args.steps, args.warmup)
+    ms_split = _timed(split, args.steps, args.warmup)
+    ms_reduce = _timed(red, args.steps, args.warmup)
+    # the same launch over each kind of work alone: the decode sequences, then the chunk
+    dec_idx = [i for i, ql in enumerate(w.q_lens) if ql == 1]
+    pre_idx = [i for i, ql in enumerate(w.q_lens) if ql > 1]
+    cu = np.concatenate([[0], np.cumsum(w.q_lens)]).astype(np.int64)
+
+    def part(idx, multi):
+        rows = torch.cat([torch.arange(int(cu[i]), int(cu[i + 1])) for i in idx]).to(dev)
+        q_p = st["q"][rows].contiguous()
+        sel = torch.tensor(idx, device=dev)
+        bt_p = st["block_tables"][sel].contiguous()
+        sl_p = st["seq_lens"][sel].contiguous()
+        cu_p = None
+        if multi:
+            cu_p = torch.tensor(np.concatenate([[0], np.cumsum([w.q_lens[i] for i in idx])]),
+                                dtype=torch.int32, device=dev)
+        ws_p = binding.SplitWorkspace(q_p.shape[0], q_p.shape[1], q_p.shape[2], ws.shape[2], dev)
+        return _timed(lambda: binding.decode_split(q_p, st["k_pool"], st["v_pool"], bt_p, sl_p,
+                                                   w.scale, partition_size=p, cu_q_lens=cu_p,
+                                                   workspace=ws_p), args.steps, args.warmup)
+
+    ms_dec = part(dec_idx, False)
+    ms_pre = part(pre_idx, True)
+    # algorithmic work: every decode key once; the chunk's K/V once, its Q in and O out
+    esize = 2
+    row = w.num_kv_heads * w.head_dim * esize * 2
+    dec = [n for n, ql in zip(w.seq_lens, w.q_lens) if ql == 1]
+    pre = [(n, ql) for n, ql in zip(w.seq_lens, w.q_lens) if ql > 1]
+    bytes_dec = sum(dec) * row + 2 * len(dec) * w.num_q_heads * w.head_dim * esize
+    bytes_pre = sum(n * row + 2 * ql * w.num_q_heads * w.head_dim * esize for n, ql in pre)
+    pairs = sum(sum(n - ql + i + 1 for i in range(ql)) for n, ql in pre)
+    flops = pairs * w.num_q_heads * 4 * w.head_dim
+    alg = bytes_dec + bytes_pre
+    t_min = max(alg / (HBM_PEAK_GBPS * 1e9), flops / 2.5e15)
+    res = {"workload": "long_context: 8 x 32768 decode + a 512-token causal chunk after 4096 "
+                       "tokens, block_size 32, 32/8 heads, head_dim 128, bf16, partitions of 512; "
+                       "one pa_decode_split launch + pa_reduce",
+           "ms": round(ms, 4), "split_ms": round(ms_split, 4), "reduce_ms": round(ms_reduce, 4),
+           "split_decode_only_ms": round(ms_dec, 4), "split_prefill_only_ms": round(ms_pre, 4),
+           "decode_only_GBps": round(bytes_dec / (ms_dec * 1e-3) / 1e9, 1),
+           "prefill_only_TFLOPs": round(flops / (ms_pre * 1e-3) / 1e12, 1),
+           "alg_bytes": int(alg), "prefill_flops": int(flops),
+           "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+           "t_min_us": round(1e6 * t_min, 1),
+           "pct_of_t_min": round(100 * t_min / (ms * 1e-3), 2)}
+    log(f"long_context: {res}")
+    del st, ws, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def _slices(ws, num_seqs, hq, d):
@@ -385,8 +490,21 @@ def _traffic(path):
     return data.get("bytes_per_launch")
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cpu_baseline(w, budget_s):
-    """The oracle as it stands, on a bounded, seeded sample of the same queries."""
+    """The oracle as it stands, on a bounded, seeded sample of the same queries: once
+    on every host core the process may use (one query per worker thread at a time;
+    NumPy releases the GIL in its array loops) and once on one thread."""
+    import concurrent.futures
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import runner as orun
@@ -395,26 +513,48 @@ def _cpu_baseline(w, budget_s):
     ost = orun.replay(w)
     log(f"oracle replay (setup, untimed) {time.time() - t0:.1f}s")
     order = np.random.default_rng(0).permutation(len(w.seq_lens)).tolist()
-    done = []  # query evaluations, in seeded order, cycling until the budget is spent
-    with threadpool_limits(limits=1):
-        start = time.perf_counter()
-        while time.perf_counter() - start < budget_s:
-            for j in order:
+    cores = len(os.sched_getaffinity(0))
+
+    def run(threads, budget):
+        done = []
+        stop = [False]
+
+        def worker(k):
+            i = k
+            while not stop[0]:
+                j = order[i % len(order)]
                 orun.attention(w, ost, tokens=[j])
                 done.append(j)
-                if time.perf_counter() - start >= budget_s:
-                    break
-        elapsed = time.perf_counter() - start
-    kv = sum(w.seq_lens[j] for j in done) * w.num_kv_heads * w.head_dim * 2 * 2
+                i += threads
+
+        with threadpool_limits(limits=1):
+            start = time.perf_counter()
+            with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+                futs = [ex.submit(worker, k) for k in range(threads)]
+                time.sleep(budget)
+                stop[0] = True
+                for f in futs:
+                    f.result()
+            elapsed = time.perf_counter() - start
+        keys = sum(w.seq_lens[j] for j in done)
+        kv = keys * w.num_kv_heads * w.head_dim * 2 * 2
+        return kv / elapsed / 1e9, len(done) / elapsed, len(done), keys, elapsed
+
+    gbps, qps, n, keys, el = run(cores, budget_s)
+    gbps1, qps1, n1, keys1, el1 = run(1, budget_s / 2)
     return {
-        "value": round(kv / elapsed / 1e9, 4),
+        "value": round(gbps, 4),
         "unit": "GB/s",
-        "queries_per_s": round(len(done) / elapsed, 2),
-        "cores": 1,
+        "queries_per_s": round(qps, 2),
+        "cores": cores,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": f"{len(done)} decode-query evaluations over the {len(w.seq_lens)} queries "
-                  f"(seeded order, repeated), {sum(w.seq_lens[j] for j in done)} keys, "
-                  f"{elapsed:.1f}s, float64 NumPy, one thread",
+        "sample": f"{n} decode-query evaluations over the {len(w.seq_lens)} queries "
+                  f"(seeded order, repeated), {keys} keys, {el:.1f}s, float64 NumPy, "
+                  f"{cores} worker threads",
+        "one_thread": {"value": round(gbps1, 4), "unit": "GB/s",
+                       "queries_per_s": round(qps1, 2),
+                       "sample": f"{n1} query evaluations, {keys1} keys, {el1:.1f}s"},
     }
 
 

@@ -190,30 +190,62 @@ pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_p
                              float* k_scale, float* v_scale, const int32_t* pairs,
                              int32_t num_pairs, void* stream);
 
-/* Split-sequence paged attention, first pass.  The keys a query sees are cut
- * into partitions of `partition_size` tokens (partition p = keys
- * [p*P, min((p+1)*P, key_end))); each partition is summarised by
- *   part_o[j, h, p, :] = softmax-weighted mean of its values   (fp32)
- *   part_lse[j, h, p]  = log(sum over its keys of exp(scale*q.k)) (natural log)
- * which pa_reduce merges.  This is the running max/sum recurrence of the
- * pages' online softmax with one partition as the unit.
+/* Split-sequence paged attention.  The first pass summarises the keys of
+ * every query by partitions; the second (pa_reduce) merges the summaries.
+ * Both share one caller-owned device workspace, sized and laid out by
+ * pa_split_workspace_layout:
+ *   part_o   at part_o_offset   fp32 [num_q_tokens, num_q_heads, max_partitions, head_dim]
+ *   part_lse at part_lse_offset fp32 [num_q_tokens, num_q_heads, max_partitions]
+ *   control  at control_offset  256 bytes of work-queue counters
+ * Entry (j, h, p) of a partition that exists for query j is
+ *   part_o   = softmax-weighted mean of the partition's values
+ *   part_lse = log(sum over its keys of exp(scale*q.k))   (natural log)
+ * -- the running max / running sum state of the pages' online softmax
+ * ("19.2 KV Cache 系统化管理" §19.2.3) with one partition as the unit.  The
+ * control block must hold zeros before the first pa_decode_split on a
+ * workspace (allocate it zeroed, e.g. hipMemset once); every call leaves it
+ * zeroed again.  Calls sharing a workspace must be ordered on one stream. */
+typedef struct {
+  size_t part_o_offset;
+  size_t part_lse_offset;
+  size_t control_offset;
+  size_t total_bytes; /* workspace bytes; offsets are 256-byte aligned */
+} pa_split_layout;
+
+pa_status pa_split_workspace_layout(int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_partitions, pa_split_layout* layout);
+/* total_bytes of the same layout, or 0 if a size is out of range. */
+size_t pa_split_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_partitions);
+
+/* First pass.  A sequence with one query token (a decode step) has its keys
+ * 0 .. seq_len-1 cut into partitions of `partition_size` tokens (partition p
+ * = keys [p*P, min((p+1)*P, seq_len)), ceil(seq_len/P) of them).  A
+ * sequence with several query tokens holds a chunk of a prefill ("LLM 推理引擎
+ * 的内存管理与调度" §8): its query tokens are its last q_len tokens, query i
+ * sits at position seq_len - q_len + i and sees keys 0 .. position (causal).
+ * Each of its queries has two partitions, keys [0, h) and [h, position],
+ * split at h = 32 * floor(ceil(ctx / 32) / 2) with ctx = seq_len - q_len
+ * (half the context cached before the chunk, in whole 32-key tiles), or
+ * one partition with all its keys when h is 0.  Only existing partitions are
+ * written.
+ *   workspace    : device memory of workspace_bytes >= total_bytes of
+ *                  pa_split_workspace_layout(num_q_tokens, num_q_heads,
+ *                  head_dim, max_partitions), 256-byte aligned
  *   q            : [num_q_tokens, num_q_heads, head_dim], pool dtype
  *   cu_q_lens    : device int32 [num_seqs+1] prefix sums of query tokens per
- *                  sequence, or NULL when each sequence has exactly one
- *                  (then num_q_tokens == num_seqs).  A sequence's query
- *                  tokens are its last q_len tokens; query i sits at
- *                  position seq_len - q_len + i and sees keys 0 .. position
- *                  (chunked prefill, "LLM 推理引擎的内存管理与调度" §8).
- *   part_o       : fp32 [num_q_tokens, num_q_heads, max_partitions, head_dim]
- *   part_lse     : fp32 [num_q_tokens, num_q_heads, max_partitions]
- * Every query has ceil(key_end/partition_size) partitions, key_end = its
- * position + 1; only those entries are written.  The queries of multi-query
- * sequences (prefill chunks) run on the matrix cores for bf16 pools (tiles of
- * 64 (token, head) rows x 32 keys, v_mfma_f32_16x16x32_bf16; probabilities
- * rounded to bf16 for the P V product) and on the vector units for fp32.
- * Requires partition_size % block_size == 0, partition_size % 16 == 0 and
- * max_partitions*partition_size >= max_blocks_per_seq*block_size. */
-pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,
+ *                  sequence, or NULL when each sequence has exactly one (then
+ *                  num_q_tokens == num_seqs)
+ * One launch runs a work list that mixes decode partitions (vector units) and
+ * prefill tiles (bf16 pools, head_dim <= 128: 128 (token, head) rows x one
+ * partition per tile on the matrix cores with v_mfma_f32_32x32x16_bf16,
+ * probabilities rounded to bf16 for the P V product; other pools: vector
+ * units), drained by persistent workgroups through the work-queue counters
+ * of the workspace's control block.
+ * Requires partition_size % block_size == 0, partition_size % 16 == 0,
+ * max_partitions*partition_size >= max_blocks_per_seq*block_size,
+ * max_partitions >= 2 when cu_q_lens is given, and num_seqs <= 8192. */
+pa_status pa_decode_split(const pa_kv_layout* layout, void* workspace, size_t workspace_bytes,
                           int32_t max_partitions, int32_t partition_size,
                           const void* q, const int32_t* cu_q_lens, int32_t num_q_tokens,
                           const void* k_pool, const void* v_pool,
@@ -221,15 +253,25 @@ pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part
                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                           float scale, void* stream);
 
-/* Split-sequence paged attention, second pass: log-sum-exp merge of the
- * partitions pa_decode_split wrote (same partition rule).  With L = log sum_p
+/* The same over fp8 pools (codes and scales as in pa_decode_fp8; bf16 q),
+ * with the same partitions; prefill queries run on the vector units. */
+pa_status pa_decode_split_fp8(const pa_kv_layout* layout, void* workspace,
+                              size_t workspace_bytes, int32_t max_partitions,
+                              int32_t partition_size, const void* q, const int32_t* cu_q_lens,
+                              int32_t num_q_tokens, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              float scale, void* stream);
+
+/* Second pass: log-sum-exp merge of the partitions pa_decode_split wrote into
+ * `workspace` (same sizes and partition rule).  With L = log sum_p
  * exp(lse_p):  out[j, h, :] = sum_p exp(lse_p - L) * o_p,  lse_out[j, h] = L.
  *   out     : [num_q_tokens, num_q_heads, head_dim] of out_dtype
  *   lse_out : fp32 [num_q_tokens, num_q_heads] or NULL
  * A query with no key gets a zero row and lse -inf. */
-pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out,
-                    const float* part_o, const float* part_lse,
-                    int32_t max_partitions, int32_t partition_size,
+pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const void* workspace,
+                    size_t workspace_bytes, int32_t max_partitions, int32_t partition_size,
                     const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
                     void* stream);

@@ -26,11 +26,16 @@ Where the pages are silent, these readings are taken (listed in the design doc):
   position ``len - q_len + i`` and sees keys ``0 .. position``.
 * A query that sees no key returns zeros.
 * Split-sequence partitions (not on the pages) apply the same running
-  max/sum recurrence with one partition as the unit: partition ``p`` covers
-  keys ``[p*P, min((p+1)*P, key_end))`` and is summarised by its normalised
-  output and its natural-log log-sum-exp of scaled scores; merging the
-  summaries with weights ``exp(lse_p - L)``, ``L = log(sum exp(lse_p))``,
-  gives back the full softmax.
+  max/sum recurrence with one partition as the unit: for a sequence with one
+  query token (a decode step), partition ``p`` covers keys
+  ``[p*P, min((p+1)*P, key_end))``; every query of a prefill chunk (a
+  sequence with several query tokens) has two partitions, keys ``[0, h)``
+  and ``[h, key_end)``, split at ``h = 32 * floor(ceil(ctx / 32) / 2)``
+  with ``ctx = len - q_len`` the context cached before the chunk, or one
+  partition with all its keys when ``h`` is 0.  A partition is summarised by its normalised output and its
+  natural-log log-sum-exp of scaled scores; merging the summaries with
+  weights ``exp(lse_p - L)``, ``L = log(sum exp(lse_p))``, gives back the
+  full softmax.
 
 Storage convention: pools, queries and new tokens are either float arrays or
 ``uint16`` arrays holding bfloat16 bit patterns; the gathered rows are
@@ -160,8 +165,28 @@ def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
     return out
 
 
-def num_partitions(key_end: int, partition_size: int) -> int:
-    return (key_end + partition_size - 1) // partition_size if key_end > 0 else 0
+def prefill_split(seq_len: int, q_len: int) -> int:
+    """Where the keys of a prefill chunk's queries are split: half of the context
+    cached before the chunk, in whole 32-key tiles (0: no split)."""
+    ctx = seq_len - q_len
+    return 32 * (((ctx + 31) // 32) // 2)
+
+
+def partition_bounds(key_end: int, partition_size: int, seq_len: int = 0, q_len: int = 1):
+    """Key ranges ``[(lo, hi), ...]`` of the partitions of a query that sees keys
+    ``0 .. key_end - 1``: ``[p*P, min((p+1)*P, key_end))`` for a decode query;
+    ``[0, h)`` and ``[h, key_end)`` for a query of a prefill chunk
+    (``q_len > 1``, ``h = prefill_split``), or ``[0, key_end)`` when ``h`` is 0."""
+    if key_end <= 0:
+        return []
+    if q_len > 1:
+        h = prefill_split(seq_len, q_len)
+        return [(0, h), (h, key_end)] if h > 0 else [(0, key_end)]
+    return [(lo, min(lo + partition_size, key_end)) for lo in range(0, key_end, partition_size)]
+
+
+def num_partitions(key_end: int, partition_size: int, seq_len: int = 0, q_len: int = 1) -> int:
+    return len(partition_bounds(key_end, partition_size, seq_len, q_len))
 
 
 def split_partials(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
@@ -176,7 +201,12 @@ def split_partials(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
     partitions are NaN.
     """
     q = np.asarray(q)
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
     positions = query_positions(seq_lens, cu_q_lens)
+    if cu_q_lens is None:
+        q_lens = np.ones(len(seq_lens), dtype=np.int64)
+    else:
+        q_lens = np.diff(np.asarray(cu_q_lens, dtype=np.int64))
     nq, hq, d = q.shape
     o = np.full((nq, hq, max_partitions, d), np.nan)
     lse = np.full((nq, hq, max_partitions), np.nan)
@@ -186,7 +216,8 @@ def split_partials(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
     for j in which:
         b, pos = positions[j]
         key_end = pos + 1
-        n = num_partitions(key_end, partition_size)
+        bounds = partition_bounds(key_end, partition_size, int(seq_lens[b]), int(q_lens[b]))
+        n = len(bounds)
         if n > max_partitions:
             raise ValueError("max_partitions too small")
         nparts[j] = n
@@ -196,8 +227,7 @@ def split_partials(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
         keys, vals = gather_kv(k_pool, v_pool, tables[b], key_end, block_size)
         s, kv_of_head = _scores(q_j, keys, scale, keys.shape[1])
         v_for_head = np.transpose(vals[:, kv_of_head, :], (1, 0, 2))
-        for p in range(n):
-            lo, hi = p * partition_size, min((p + 1) * partition_size, key_end)
+        for p, (lo, hi) in enumerate(bounds):
             sp = s[:, lo:hi]
             m = sp.max(axis=1, keepdims=True)
             e = np.exp(sp - m)

@@ -62,9 +62,14 @@ _SIGNATURES = {
                              _p, ctypes.c_size_t, _p]),
     "pa_copy_blocks_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p]),
     "pa_swap_blocks": (_i32, [_LAYOUT, _p, _p, _p, _p, _i32, _p, _i32, _p]),
-    "pa_decode_split": (_i32, [_LAYOUT, _p, _p, _i32, _i32, _p, _p, _i32, _p, _p, _p, _i32, _p,
-                               _i32, _i32, _f32, _p]),
-    "pa_reduce": (_i32, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _p]),
+    "pa_split_workspace_layout": (_i32, [_i32, _i32, _i32, _i32, ctypes.c_void_p]),
+    "pa_split_workspace_bytes": (ctypes.c_size_t, [_i32, _i32, _i32, _i32]),
+    "pa_decode_split": (_i32, [_LAYOUT, _p, ctypes.c_size_t, _i32, _i32, _p, _p, _i32, _p, _p,
+                               _p, _i32, _p, _i32, _i32, _f32, _p]),
+    "pa_decode_split_fp8": (_i32, [_LAYOUT, _p, ctypes.c_size_t, _i32, _i32, _p, _p, _i32, _p,
+                                   _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p]),
+    "pa_reduce": (_i32, [_p, _i32, _p, _p, ctypes.c_size_t, _i32, _i32, _p, _p, _i32, _i32, _i32,
+                         _i32, _p]),
     "pa_pool_create": (_i32, [_i32, _i32, _pi32, ctypes.POINTER(_p)]),
     "pa_pool_destroy": (None, [_p]),
     "pa_pool_num_free": (_i32, [_p]),
@@ -322,64 +327,140 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, wo
     return out
 
 
-def max_partitions_for(max_blocks: int, block_size: int, partition_size: int) -> int:
-    return max(1, -(-(max_blocks * block_size) // partition_size))
+def max_partitions_for(max_blocks: int, block_size: int, partition_size: int,
+                       prefill: bool = False) -> int:
+    """Partitions a split workspace needs: the decode queries' ceil(capacity / P),
+    and at least two when prefill chunks (``cu_q_lens``) are present."""
+    return max(2 if prefill else 1, -(-(max_blocks * block_size) // partition_size))
 
 
-def decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
-                 partition_size: int = 512, cu_q_lens=None, part_o=None, part_lse=None,
-                 max_partitions=None):
-    """``pa_decode_split``: per-partition summaries.  Returns ``(part_o, part_lse)``."""
-    lay, kp, vp = _pools(k_pool, v_pool)
-    if q.dim() != 3 or q.shape[2] != lay.head_dim:
+class SplitLayout(ctypes.Structure):
+    _fields_ = [("part_o_offset", ctypes.c_size_t), ("part_lse_offset", ctypes.c_size_t),
+                ("control_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t)]
+
+
+class SplitWorkspace:
+    """Device workspace of the split path, laid out by ``pa_split_workspace_layout``.
+
+    ``part_o`` / ``part_lse`` are views of its partial buffers; the control
+    block starts zeroed (the library leaves it zeroed after every call).
+    """
+
+    def __init__(self, num_q_tokens: int, num_q_heads: int, head_dim: int,
+                 max_partitions: int, device):
+        lay = SplitLayout()
+        _check(lib().pa_split_workspace_layout(int(num_q_tokens), int(num_q_heads),
+                                               int(head_dim), int(max_partitions),
+                                               ctypes.byref(lay)))
+        self.shape = (int(num_q_tokens), int(num_q_heads), int(max_partitions), int(head_dim))
+        self.layout = lay
+        self.buffer = torch.zeros(lay.total_bytes, dtype=torch.uint8, device=device)
+        n_o = int(np.prod(self.shape))
+        self.part_o = self.buffer[lay.part_o_offset:lay.part_o_offset + 4 * n_o] \
+            .view(torch.float32).view(self.shape)
+        n_l = n_o // self.shape[3]
+        self.part_lse = self.buffer[lay.part_lse_offset:lay.part_lse_offset + 4 * n_l] \
+            .view(torch.float32).view(self.shape[:3])
+
+    def ptr(self):
+        return ctypes.c_void_p(self.buffer.data_ptr()), self.layout.total_bytes
+
+
+def split_workspace_bytes(num_q_tokens, num_q_heads, head_dim, max_partitions) -> int:
+    """``pa_split_workspace_bytes``."""
+    return int(lib().pa_split_workspace_bytes(int(num_q_tokens), int(num_q_heads),
+                                              int(head_dim), int(max_partitions)))
+
+
+def _split_args(q, block_tables, seq_lens, cu_q_lens, head_dim):
+    if q.dim() != 3 or q.shape[2] != head_dim:
         raise ValueError("q must be [num_q_tokens, num_q_heads, head_dim]")
-    nq, hq = int(q.shape[0]), int(q.shape[1])
     b = int(seq_lens.shape[0])
     bt, mb, sl = _tables(block_tables, seq_lens, b)
     if cu_q_lens is not None and tuple(cu_q_lens.shape) != (b + 1,):
         raise ValueError("cu_q_lens must be [num_seqs + 1]")
-    if max_partitions is None:
-        max_partitions = max_partitions_for(mb, lay.block_size, partition_size)
-    shape_o = (nq, hq, max_partitions, lay.head_dim)
-    if part_o is None:
-        part_o = torch.empty(shape_o, dtype=torch.float32, device=q.device)
-    if part_lse is None:
-        part_lse = torch.empty(shape_o[:3], dtype=torch.float32, device=q.device)
-    if tuple(part_o.shape) != shape_o or tuple(part_lse.shape) != shape_o[:3]:
-        raise ValueError("partial buffers have the wrong shape")
-    _check(lib().pa_decode_split(ctypes.byref(lay), _dev(part_o, "part_o", torch.float32),
-                                 _dev(part_lse, "part_lse", torch.float32), int(max_partitions),
-                                 int(partition_size), _dev(q, "q", k_pool.dtype),
-                                 _opt(cu_q_lens, "cu_q_lens", torch.int32), nq, kp, vp, bt, mb, sl,
-                                 b, hq, float(scale), _stream()))
-    return part_o, part_lse
+    return b, bt, mb, sl
 
 
-def reduce(part_o, part_lse, seq_lens, partition_size: int, out_dtype=torch.bfloat16,
+def _workspace_for(workspace, q, mb, block_size, partition_size, max_partitions, prefill):
+    nq, hq, d = (int(x) for x in q.shape)
+    if workspace is None:
+        if max_partitions is None:
+            max_partitions = max_partitions_for(mb, block_size, partition_size, prefill)
+        workspace = SplitWorkspace(nq, hq, d, max_partitions, q.device)
+    elif workspace.shape[:2] != (nq, hq) or workspace.shape[3] != d:
+        raise ValueError("workspace was made for other sizes")
+    return workspace
+
+
+def decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
+                 partition_size: int = 512, cu_q_lens=None, workspace=None,
+                 max_partitions=None) -> SplitWorkspace:
+    """``pa_decode_split``: per-partition summaries in a :class:`SplitWorkspace`."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    b, bt, mb, sl = _split_args(q, block_tables, seq_lens, cu_q_lens, lay.head_dim)
+    ws = _workspace_for(workspace, q, mb, lay.block_size, partition_size, max_partitions,
+                        cu_q_lens is not None)
+    wp, wn = ws.ptr()
+    _check(lib().pa_decode_split(ctypes.byref(lay), wp, wn, ws.shape[2], int(partition_size),
+                                 _dev(q, "q", k_pool.dtype),
+                                 _opt(cu_q_lens, "cu_q_lens", torch.int32), int(q.shape[0]), kp,
+                                 vp, bt, mb, sl, b, int(q.shape[1]), float(scale), _stream()))
+    return ws
+
+
+def decode_split_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, scale: float,
+                     partition_size: int = 512, cu_q_lens=None, workspace=None,
+                     max_partitions=None) -> SplitWorkspace:
+    """``pa_decode_split_fp8``: the split first pass over e4m3 pools (bf16 ``q``)."""
+    lay, kp, vp, ks, vs = _fp8_pools(k_pool, v_pool, k_scale, v_scale)
+    b, bt, mb, sl = _split_args(q, block_tables, seq_lens, cu_q_lens, lay.head_dim)
+    ws = _workspace_for(workspace, q, mb, lay.block_size, partition_size, max_partitions,
+                        cu_q_lens is not None)
+    wp, wn = ws.ptr()
+    _check(lib().pa_decode_split_fp8(ctypes.byref(lay), wp, wn, ws.shape[2], int(partition_size),
+                                     _dev(q, "q", torch.bfloat16),
+                                     _opt(cu_q_lens, "cu_q_lens", torch.int32), int(q.shape[0]),
+                                     kp, vp, ks, vs, bt, mb, sl, b, int(q.shape[1]),
+                                     float(scale), _stream()))
+    return ws
+
+
+def reduce(workspace: SplitWorkspace, seq_lens, partition_size: int, out_dtype=torch.bfloat16,
            cu_q_lens=None, out=None, lse_out=None):
     """``pa_reduce``: log-sum-exp merge of the partitions.  Returns ``out``."""
-    nq, hq, maxp, d = (int(x) for x in part_o.shape)
+    nq, hq, maxp, d = workspace.shape
     b = int(seq_lens.shape[0])
+    dev = workspace.buffer.device
     if out is None:
-        out = torch.empty((nq, hq, d), dtype=out_dtype, device=part_o.device)
-    if out.dtype not in _DTYPES or tuple(out.shape) != (nq, hq, d):
+        out = torch.empty((nq, hq, d), dtype=out_dtype, device=dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or tuple(out.shape) != (nq, hq, d):
         raise ValueError("out must be [num_q_tokens, num_q_heads, head_dim] f32/bf16")
+    wp, wn = workspace.ptr()
     _check(lib().pa_reduce(_dev(out, "out"), _DTYPES[out.dtype],
-                           _opt(lse_out, "lse_out", torch.float32),
-                           _dev(part_o, "part_o", torch.float32),
-                           _dev(part_lse, "part_lse", torch.float32), maxp, int(partition_size),
-                           _opt(cu_q_lens, "cu_q_lens", torch.int32),
+                           _opt(lse_out, "lse_out", torch.float32), wp, wn, maxp,
+                           int(partition_size), _opt(cu_q_lens, "cu_q_lens", torch.int32),
                            _dev(seq_lens, "seq_lens", torch.int32), b, nq, hq, d, _stream()))
     return out
 
 
 def paged_attention(q, k_pool, v_pool, block_tables, seq_lens, scale: float,
-                    partition_size: int = 512, cu_q_lens=None):
+                    partition_size: int = 512, cu_q_lens=None, workspace=None, out=None):
     """Split pass + reduce: attention output of every query token."""
-    part_o, part_lse = decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale,
-                                    partition_size=partition_size, cu_q_lens=cu_q_lens)
-    return reduce(part_o, part_lse, seq_lens, partition_size, out_dtype=q.dtype,
-                  cu_q_lens=cu_q_lens)
+    ws = decode_split(q, k_pool, v_pool, block_tables, seq_lens, scale,
+                      partition_size=partition_size, cu_q_lens=cu_q_lens, workspace=workspace)
+    return reduce(ws, seq_lens, partition_size, out_dtype=q.dtype, cu_q_lens=cu_q_lens, out=out)
+
+
+def paged_attention_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens,
+                        scale: float, partition_size: int = 512, cu_q_lens=None,
+                        workspace=None, out=None):
+    """Split pass + reduce over e4m3 pools: bf16 output of every query token."""
+    ws = decode_split_fp8(q, k_pool, v_pool, k_scale, v_scale, block_tables, seq_lens, scale,
+                          partition_size=partition_size, cu_q_lens=cu_q_lens,
+                          workspace=workspace)
+    return reduce(ws, seq_lens, partition_size, out_dtype=torch.bfloat16, cu_q_lens=cu_q_lens,
+                  out=out)
 
 
 # --- host block pool ------------------------------------------------------------

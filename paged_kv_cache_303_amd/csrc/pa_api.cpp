@@ -132,7 +132,7 @@ static pa_status fill_decode_args(const char* what, const pa_kv_layout* layout, 
   a->partition_size = 0;
   a->max_partitions = 1;
   a->waves_per_group = pa::waves_per_group(layout->num_kv_heads);
-  a->prefill_mfma = 0;
+  a->queue = nullptr;
   return PA_OK;
 }
 
@@ -247,7 +247,7 @@ static pa_status decode_launch(const char* what, pa::DecodeArgs& a, void* out, v
       return pa::launch_status(pa::launch_decode_stream(a, s, stream), what);
     }
   }
-  return pa::launch_status(pa::launch_decode(a, false, stream), what);
+  return pa::launch_status(pa::launch_decode(a, stream), what);
 }
 
 extern "C" {
@@ -317,8 +317,8 @@ pa_status pa_swap_blocks(const pa_kv_layout* dst_layout, void* dst_k, void* dst_
   if (dst_layout->dtype != PA_F32 && dst_layout->dtype != PA_BF16 && dst_layout->dtype != PA_FP8)
     return fail(PA_ERR_UNSUPPORTED, "%s: unknown dtype %d", what, dst_layout->dtype);
   if ((int64_t)dst_layout->block_size * dst_layout->num_kv_heads * dst_layout->head_dim *
-          pa::elt_bytes(dst_layout->dtype) % 16 != 0)
-    return fail(PA_ERR_UNSUPPORTED, "%s: a block must be a multiple of 16 bytes", what);
+          pa::elt_bytes(dst_layout->dtype) % 4 != 0)
+    return fail(PA_ERR_UNSUPPORTED, "%s: a block must be a multiple of 4 bytes", what);
   if (src_num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "%s: src_num_blocks must be > 0", what);
   if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_pairs < 0", what);
   if (num_pairs == 0) return PA_OK;
@@ -359,7 +359,116 @@ pa_status pa_copy_blocks_fp8(const pa_kv_layout* layout, void* k_pool, void* v_p
       pa::launch_copy_blocks(sc, k_scale, v_scale, pairs, num_pairs, stream), what);
 }
 
-pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part_lse,
+}  // extern "C"
+
+namespace {
+
+// Workspace of the split path: partial outputs, partial lse values and the
+// work-queue counters, each 256-byte aligned.  false if a size is out of range.
+bool split_layout(int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                  int32_t max_partitions, pa_split_layout* l) {
+  if (num_q_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || max_partitions <= 0) return false;
+  const uint64_t rows = (uint64_t)num_q_tokens * (uint64_t)num_q_heads * (uint64_t)max_partitions;
+  if (rows > ((uint64_t)1 << 40) / (uint64_t)head_dim) return false;
+  const size_t o_bytes = align256((size_t)(rows * (uint64_t)head_dim * sizeof(float)));
+  const size_t lse_bytes = align256((size_t)(rows * sizeof(float)));
+  l->part_o_offset = 0;
+  l->part_lse_offset = o_bytes;
+  l->control_offset = o_bytes + lse_bytes;
+  l->total_bytes = o_bytes + lse_bytes + 256;
+  return true;
+}
+
+// The partial buffers of a split workspace, after checking its size and alignment.
+pa_status split_buffers(const char* what, const void* workspace, size_t workspace_bytes,
+                        int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                        int32_t max_partitions, float** part_o, float** part_lse,
+                        int32_t** control) {
+  pa_split_layout l;
+  if (!split_layout(num_q_tokens, num_q_heads, head_dim, max_partitions, &l))
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace sizes out of range", what);
+  if (!workspace) return fail(PA_ERR_INVALID_ARG, "%s: workspace is NULL", what);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", what);
+  if (workspace_bytes < l.total_bytes)
+    return fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < %zu needed", what,
+                workspace_bytes, l.total_bytes);
+  char* ws = (char*)workspace;
+  *part_o = (float*)(ws + l.part_o_offset);
+  *part_lse = (float*)(ws + l.part_lse_offset);
+  if (control) *control = (int32_t*)(ws + l.control_offset);
+  return PA_OK;
+}
+
+}  // namespace
+
+// pa_decode_split / pa_decode_split_fp8 after their own argument checks.
+static pa_status split_launch(const char* what, const pa_kv_layout* layout, pa::DecodeArgs& a,
+                              void* workspace, size_t workspace_bytes, int32_t max_partitions,
+                              int32_t partition_size, const int32_t* cu_q_lens,
+                              int32_t num_q_tokens, int32_t max_blocks_per_seq, void* stream) {
+  if (num_q_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_q_tokens < 0", what);
+  if (!cu_q_lens && num_q_tokens != a.num_seqs)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: without cu_q_lens num_q_tokens (%d) must equal num_seqs (%d)", what,
+                num_q_tokens, a.num_seqs);
+  if (cu_q_lens && a.num_seqs == 0 && num_q_tokens != 0)
+    return fail(PA_ERR_INVALID_ARG, "%s: query tokens without sequences", what);
+  if (a.num_seqs > pa::kSplitMaxSeqs)
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than %d sequences in one call", what,
+                pa::kSplitMaxSeqs);
+  if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % layout->block_size != 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: partition_size %d must be a positive multiple of 16 and of block_size %d",
+                what, partition_size, layout->block_size);
+  if (max_partitions <= 0 || max_partitions > 65535)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_partitions must be in [1, 65535]", what);
+  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * layout->block_size)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: max_partitions*partition_size (%lld) < max_blocks_per_seq*block_size (%lld)",
+                what, (long long)max_partitions * partition_size,
+                (long long)max_blocks_per_seq * layout->block_size);
+  if (cu_q_lens && max_partitions < 2)
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: with cu_q_lens (prefill chunks have two partitions) max_partitions must be >= 2",
+                what);
+  if ((int64_t)num_q_tokens * max_partitions * layout->num_kv_heads > (int64_t)INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "%s: too many (query, partition, KV head) units", what);
+  if (num_q_tokens == 0) return PA_OK;
+  float *part_o = nullptr, *part_lse = nullptr;
+  int32_t* control = nullptr;
+  if (pa_status st = split_buffers(what, workspace, workspace_bytes, num_q_tokens, a.num_q_heads,
+                                   a.head_dim, max_partitions, &part_o, &part_lse, &control))
+    return st;
+  a.cu_q_lens = cu_q_lens;
+  a.num_q_tokens = num_q_tokens;
+  a.part_o = part_o;
+  a.part_lse = part_lse;
+  a.queue = control;
+  a.partition_size = partition_size;
+  a.max_partitions = max_partitions;
+  return pa::launch_status(pa::launch_split(a, stream), what);
+}
+
+extern "C" {
+
+pa_status pa_split_workspace_layout(int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                                    int32_t max_partitions, pa_split_layout* layout) {
+  const char* what = "pa_split_workspace_layout";
+  if (!layout) return fail(PA_ERR_INVALID_ARG, "%s: layout is NULL", what);
+  if (!split_layout(num_q_tokens, num_q_heads, head_dim, max_partitions, layout))
+    return fail(PA_ERR_INVALID_ARG, "%s: sizes out of range", what);
+  return PA_OK;
+}
+
+size_t pa_split_workspace_bytes(int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_partitions) {
+  pa_split_layout l;
+  if (!split_layout(num_q_tokens, num_q_heads, head_dim, max_partitions, &l)) return 0;
+  return l.total_bytes;
+}
+
+pa_status pa_decode_split(const pa_kv_layout* layout, void* workspace, size_t workspace_bytes,
                           int32_t max_partitions, int32_t partition_size, const void* q,
                           const int32_t* cu_q_lens, int32_t num_q_tokens, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables,
@@ -372,42 +481,38 @@ pa_status pa_decode_split(const pa_kv_layout* layout, float* part_o, float* part
                                       &a))
     return st;
   if (layout->dtype == PA_FP8)
-    return fail(PA_ERR_UNSUPPORTED, "%s: fp8 pools are decoded by pa_decode_fp8", what);
-  if (num_q_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_q_tokens < 0", what);
-  if (!cu_q_lens && num_q_tokens != num_seqs)
-    return fail(PA_ERR_INVALID_ARG,
-                "%s: without cu_q_lens num_q_tokens (%d) must equal num_seqs (%d)", what,
-                num_q_tokens, num_seqs);
-  if (cu_q_lens && num_seqs == 0 && num_q_tokens != 0)
-    return fail(PA_ERR_INVALID_ARG, "%s: query tokens without sequences", what);
-  if (partition_size <= 0 || partition_size % 16 != 0 || partition_size % layout->block_size != 0)
-    return fail(PA_ERR_INVALID_ARG,
-                "%s: partition_size %d must be a positive multiple of 16 and of block_size %d",
-                what, partition_size, layout->block_size);
-  if (max_partitions <= 0 || max_partitions > 65535)
-    return fail(PA_ERR_INVALID_ARG, "%s: max_partitions must be in [1, 65535]", what);
-  if ((int64_t)max_partitions * partition_size < (int64_t)max_blocks_per_seq * layout->block_size)
-    return fail(PA_ERR_INVALID_ARG,
-                "%s: max_partitions*partition_size (%lld) < max_blocks_per_seq*block_size (%lld)",
-                what, (long long)max_partitions * partition_size,
-                (long long)max_blocks_per_seq * layout->block_size);
-  if (num_q_tokens == 0) return PA_OK;
-  if (!part_o || !part_lse) return fail(PA_ERR_INVALID_ARG, "%s: NULL partial buffer", what);
-  a.cu_q_lens = cu_q_lens;
-  a.num_q_tokens = num_q_tokens;
-  a.part_o = part_o;
-  a.part_lse = part_lse;
-  a.partition_size = partition_size;
-  a.max_partitions = max_partitions;
-  a.prefill_mfma = pa::prefill_mfma_supported(a) ? 1 : 0;
-  if (pa_status st = pa::launch_status(pa::launch_decode(a, true, stream), what)) return st;
-  if (a.prefill_mfma)
-    return pa::launch_status(pa::launch_prefill_mfma(a, stream), what);
-  return PA_OK;
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools need their scales: use pa_decode_split_fp8",
+                what);
+  return split_launch(what, layout, a, workspace, workspace_bytes, max_partitions,
+                      partition_size, cu_q_lens, num_q_tokens, max_blocks_per_seq, stream);
 }
 
-pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const float* part_o,
-                    const float* part_lse, int32_t max_partitions, int32_t partition_size,
+pa_status pa_decode_split_fp8(const pa_kv_layout* layout, void* workspace,
+                              size_t workspace_bytes, int32_t max_partitions,
+                              int32_t partition_size, const void* q, const int32_t* cu_q_lens,
+                              int32_t num_q_tokens, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              float scale, void* stream) {
+  const char* what = "pa_decode_split_fp8";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (layout->dtype != PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: layout dtype must be PA_FP8", what);
+  if (num_seqs > 0 && (!k_scale || !v_scale))
+    return fail(PA_ERR_INVALID_ARG, "%s: NULL scale pool", what);
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return split_launch(what, layout, a, workspace, workspace_bytes, max_partitions,
+                      partition_size, cu_q_lens, num_q_tokens, max_blocks_per_seq, stream);
+}
+
+pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const void* workspace,
+                    size_t workspace_bytes, int32_t max_partitions, int32_t partition_size,
                     const int32_t* cu_q_lens, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t num_q_tokens, int32_t num_q_heads, int32_t head_dim, void* stream) {
   const char* what = "pa_reduce";
@@ -423,8 +528,11 @@ pa_status pa_reduce(void* out, int32_t out_dtype, float* lse_out, const float* p
     return fail(PA_ERR_INVALID_ARG, "%s: without cu_q_lens num_q_tokens must equal num_seqs", what);
   if (num_q_tokens == 0) return PA_OK;
   if (num_seqs == 0) return fail(PA_ERR_INVALID_ARG, "%s: query tokens without sequences", what);
-  if (!out || !part_o || !part_lse || !seq_lens)
-    return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  if (!out || !seq_lens) return fail(PA_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  float *part_o = nullptr, *part_lse = nullptr;
+  if (pa_status st = split_buffers(what, workspace, workspace_bytes, num_q_tokens, num_q_heads,
+                                   head_dim, max_partitions, &part_o, &part_lse, nullptr))
+    return st;
   pa::ReduceArgs a;
   a.out = out;
   a.lse_out = lse_out;

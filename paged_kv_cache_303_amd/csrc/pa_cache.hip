@@ -81,6 +81,41 @@ __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
 
 constexpr int64_t kCopyChunk = 16384;  // bytes per workgroup
 
+// Bytes [lo, hi) of one K block and one V block.  Blocks whose size is a
+// multiple of 16 bytes (every K/V pool) go in 16-byte lanes; others (the fp8
+// scale pools hold block_size * kv_heads float32 values, so a block may be 8
+// bytes, and its start only 4-byte aligned) go in 4-byte words.
+__device__ __forceinline__ void copy_span(char* __restrict__ dk, char* __restrict__ dv,
+                                          const char* __restrict__ sk,
+                                          const char* __restrict__ sv, int64_t lo, int64_t hi,
+                                          bool words16) {
+  if (words16) {
+    const int64_t n16 = (hi - lo) >> 4;
+    const uint4* a = (const uint4*)(sk + lo);
+    const uint4* b = (const uint4*)(sv + lo);
+    uint4* c = (uint4*)(dk + lo);
+    uint4* d = (uint4*)(dv + lo);
+    for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
+      const uint4 x = a[i];
+      const uint4 y = b[i];
+      c[i] = x;
+      d[i] = y;
+    }
+    return;
+  }
+  const int64_t n4 = (hi - lo) >> 2;
+  const uint32_t* a = (const uint32_t*)(sk + lo);
+  const uint32_t* b = (const uint32_t*)(sv + lo);
+  uint32_t* c = (uint32_t*)(dk + lo);
+  uint32_t* d = (uint32_t*)(dv + lo);
+  for (int64_t i = threadIdx.x; i < n4; i += blockDim.x) {
+    const uint32_t x = a[i];
+    const uint32_t y = b[i];
+    c[i] = x;
+    d[i] = y;
+  }
+}
+
 __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp, char* __restrict__ vp,
                                                           const int32_t* __restrict__ pairs,
                                                           int64_t block_bytes, int32_t num_blocks,
@@ -90,19 +125,9 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp,
   const int32_t src = pairs[2 * pair];
   const int32_t dst = pairs[2 * pair + 1];
   if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  const int64_t lo = chunk * kCopyChunk;
-  const int64_t hi = min(lo + kCopyChunk, block_bytes);
-  const int64_t n16 = (hi - lo) >> 4;
-  const uint4* sk = (const uint4*)(kp + src * block_bytes + lo);
-  const uint4* sv = (const uint4*)(vp + src * block_bytes + lo);
-  uint4* dk = (uint4*)(kp + dst * block_bytes + lo);
-  uint4* dv = (uint4*)(vp + dst * block_bytes + lo);
-  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
-    const uint4 a = sk[i];
-    const uint4 b = sv[i];
-    dk[i] = a;
-    dv[i] = b;
-  }
+  copy_span(kp + dst * block_bytes, vp + dst * block_bytes, kp + src * block_bytes,
+            vp + src * block_bytes, chunk * kCopyChunk, min((chunk + 1) * kCopyChunk, block_bytes),
+            (block_bytes & 15) == 0);
 }
 
 // One wave per (query token, query head); kReduceWaves heads per workgroup.
@@ -127,8 +152,14 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
   }
   const int len = max(a.seq_lens[b], 0);
   const int key_end = len - q_len + (j - q_first) + 1;
+  // a decode query has ceil(key_end / P) partitions; each query of a prefill
+  // chunk (q_len > 1) has two split at half the cached context (in 32-key
+  // tiles), or one when that half is empty
   int nparts = 0;
-  if (key_end > 0) nparts = (key_end + a.partition_size - 1) / a.partition_size;
+  if (key_end > 0) {
+    if (q_len > 1) nparts = 32 * (((len - q_len + 31) / 32) / 2) > 0 ? 2 : 1;
+    else nparts = (key_end + a.partition_size - 1) / a.partition_size;
+  }
   nparts = min(nparts, a.max_partitions);
 
   const int D = a.head_dim;
@@ -181,19 +212,9 @@ __global__ __launch_bounds__(256) void swap_blocks_kernel(
   const int32_t src = pairs[2 * pair];
   const int32_t dst = pairs[2 * pair + 1];
   if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
-  const int64_t lo = chunk * kCopyChunk;
-  const int64_t hi = min(lo + kCopyChunk, block_bytes);
-  const int64_t n16 = (hi - lo) >> 4;
-  const uint4* a = (const uint4*)(sk + src * block_bytes + lo);
-  const uint4* b = (const uint4*)(sv + src * block_bytes + lo);
-  uint4* c = (uint4*)(dk + dst * block_bytes + lo);
-  uint4* d = (uint4*)(dv + dst * block_bytes + lo);
-  for (int64_t i = threadIdx.x; i < n16; i += blockDim.x) {
-    const uint4 x = a[i];
-    const uint4 y = b[i];
-    c[i] = x;
-    d[i] = y;
-  }
+  copy_span(dk + dst * block_bytes, dv + dst * block_bytes, sk + src * block_bytes,
+            sv + src * block_bytes, chunk * kCopyChunk, min((chunk + 1) * kCopyChunk, block_bytes),
+            (block_bytes & 15) == 0);
 }
 
 inline int64_t elt_size(int32_t dtype) {

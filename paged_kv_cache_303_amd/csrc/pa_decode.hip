@@ -35,654 +35,38 @@
 //     and get probability exactly 0, so NaN-poisoned tails never reach sums.
 #include <type_traits>
 
-#include "pa_device.h"
-#include "pa_launch.h"
+#include "pa_wave.h"
 
 namespace pa {
 namespace {
-
-constexpr int kMaxWaves = 8;  // workgroup = up to 8 KV heads
-
-// Index of the wave in its workgroup, as a scalar: the compiler cannot tell
-// that threadIdx.x / 64 is the same on every lane of a wave, and values
-// derived from it would otherwise live in vector registers and turn the
-// branches on them into exec-masked code.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-}
-
-template <typename T>
-struct Elt;
-template <>
-struct Elt<float> {
-  static constexpr int kVec = 4;  // elements per 16-byte load
-};
-template <>
-struct Elt<uint16_t> {  // bfloat16 bit patterns
-  static constexpr int kVec = 8;
-};
-template <>
-struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
-  static constexpr int kVec = 16;
-};
-
-#ifndef PA_TILE_TOKENS
-#define PA_TILE_TOKENS 16  // target tokens per tile (per wave, per KV head)
-#endif
-#ifndef PA_FP8_TILE_TOKENS
-#define PA_FP8_TILE_TOKENS 32  // the same for e4m3 pools (half the bytes per row)
-#endif
-#ifndef PA_MAX_CPL
-#define PA_MAX_CPL 2  // 16-byte chunks of a row per lane, at most
-#endif
-#ifndef PA_MAX_TILE_LOADS
-#define PA_MAX_TILE_LOADS 8  // 16-byte loads per lane per tile (K or V), hot shapes
-#endif
-
-// Lane layout for (element type, head_dim, query heads per KV head):
-//   CPL  16-byte chunks of a row per lane (2 halves the row reduction and the
-//        redundant exponentials; 1 when G is large, to bound accumulators)
-//   LPR  lanes per token row, TPI rows per load instruction
-//   NI   load instructions (of CPL chunks each) per tile, TT tokens per tile
-template <typename T, int D, int G, bool UNIFORM = true, int TILE = 0>
-struct Shape {
-  static constexpr int VEC = Elt<T>::kVec;
-  static constexpr int CHUNKS = D / VEC;
-  // (fp8: one chunk of 16 codes per lane already needs 16 accumulators per head)
-  static constexpr int CPL = (CHUNKS >= 8 && G <= 4 && PA_MAX_CPL >= 2 && sizeof(T) > 1) ? 2 : 1;
-  static constexpr int LPR = CHUNKS / CPL;
-  static constexpr int TPI = kWave / LPR;
-  // Loads per lane per tile (K or V; two tiles are in registers at a time):
-  // the bf16 shapes with small G get the full budget, the others less, so
-  // that accumulators and both tiles stay in 256 VGPRs without spilling.
-  static constexpr int MAX_LOADS =
-      (sizeof(T) <= 2 && G <= 4 && D <= 128 && UNIFORM) ? PA_MAX_TILE_LOADS
-      : (G >= 8 ? PA_MAX_TILE_LOADS / 4 : PA_MAX_TILE_LOADS / 2);
-  // target tokens per tile: TILE if given, else the default of the type
-  static constexpr int TILE_TOKENS =
-      TILE > 0 ? TILE : (sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : PA_TILE_TOKENS);
-  static constexpr int NI0 = (TILE_TOKENS / TPI) < 1 ? 1 : (TILE_TOKENS / TPI);
-  static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
-  static constexpr int TT = NI * TPI;
-  // Ranges start at multiples of 16 (partitions) or of TT (slices), plus
-  // multiples of TT, so every load instruction starts on a multiple of TPI
-  // (needed by the UNIFORM lookup).
-  static_assert(LPR * CPL * VEC == D && LPR <= kWave && (16 % TPI) == 0 && NI >= 1,
-                "unsupported lane layout");
-};
-
-// Lazy rescaling: the running maximum m (log2 domain) is only moved when a
-// tile's maximum exceeds it by more than this, so probabilities stay below
-// 2^kLazy and the O(G*D) rescale of the accumulators is rare.  The result
-// is independent of m up to rounding (acc and l carry the same factor).
-constexpr float kLazy = 8.0f;
-constexpr float kLn2 = 0.69314718055994530942f;
-
-// Per-wave state and tile machinery for one KV head and its G query heads.
-// UNIFORM: the rows of one load instruction always share a block (the block
-// size is a multiple of TPI), so block-table entries are wave-uniform scalar
-// loads; otherwise every lane looks its block up.
-template <typename T, int D, int G, bool UNIFORM, int TILE = 0>
-struct WaveCtx {
-  using S = Shape<T, D, G, UNIFORM, TILE>;
-  static constexpr int VEC = S::VEC, CPL = S::CPL, LPR = S::LPR, LOG_LPR = ilog2(S::LPR);
-  static constexpr int TPI = S::TPI, NI = S::NI, TT = S::TT;
-  static constexpr bool BF16 = sizeof(T) == 2;
-  // fp8 pools: e4m3 codes with one fp32 scale per (token, KV head) for K and
-  // V; the query and the output are bfloat16
-  static constexpr bool FP8 = sizeof(T) == 1;
-  static constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
-  static constexpr int QW = FP8 ? 2 : 1;  // 16-byte pieces of one chunk of the bf16 query
-  // fp8 with up to 4 heads per KV head and head_dim <= 128: the query in
-  // registers (see qf); otherwise in LDS like the other types (registers
-  // would not hold it)
-  static constexpr bool QREG = FP8 && G <= 4 && D <= 128;
-
-  struct Tile {
-    uint4 k[NI][CPL];
-    uint4 v[NI][CPL];
-    float ks[FP8 ? NI : 1], vs[FP8 ? NI : 1];  // fp8: scales of the lane's rows
-  };
-
-  // The current query lives in LDS, not registers: [G][CPL][LPR] 16-byte
-  // chunks per wave (fp32: pre-scaled), read back once per tile; the lanes
-  // of one chunk column read the same address (broadcast).  (fp8: registers,
-  // see qf.)
-  static constexpr int kQChunks = QREG ? 1 : G * CPL * LPR * QW;
-
-  const DecodeArgs& a;
-  uint4* qs;  // this wave's kQChunks chunks in LDS
-  int lane, tg, c, kvh;
-  uint32_t row_bytes, lane_col;
-  int64_t block_bytes;
-  int nb_max, bs_mask;
-  float qk_scale;
-  float m_run[G], l_run[G], acc[G][CPL][VEC];
-  // fp8: the current query's 16 dims of this lane's chunk, per head, as floats
-  // (held in registers for the whole sequence: each K chunk is converted once
-  // per tile and dotted with all G heads)
-  float qf[QREG ? G : 1][QREG ? 16 : 1];
-
-  __device__ WaveCtx(const DecodeArgs& args, int kv_head, uint4* q_lds)
-      : a(args), qs(q_lds), kvh(kv_head) {
-    lane = threadIdx.x & (kWave - 1);
-    tg = lane / LPR;
-    c = lane % LPR;
-    row_bytes = (uint32_t)a.num_kv_heads * D * sizeof(T);
-    block_bytes = (int64_t)row_bytes << a.log2_bs;
-    lane_col = (uint32_t)(kvh * D + c * VEC) * sizeof(T);
-    nb_max = a.num_blocks - 1;
-    bs_mask = (1 << a.log2_bs) - 1;
-    qk_scale = (BF16 || FP8) ? a.scale_log2 : 1.0f;  // fp32 queries are pre-scaled
-  }
-
-  // Query token j's chunks of the G heads into LDS; scores stay unscaled and
-  // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
-  __device__ void load_query(int j) {
-    if constexpr (QREG) {  // bf16 query: every lane widens its chunk's 16 dims per head
-      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int h = 0; h < QW; ++h) {
-          const uint4 v = *(const uint4*)(qrow + (int64_t)g * D + c * VEC + h * 8);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qf[g][8 * h + 2 * e] = bf16_lo(w[e]);
-            qf[g][8 * h + 2 * e + 1] = bf16_hi(w[e]);
-          }
-        }
-      return;
-    }
-    if constexpr (FP8) {  // bf16 query in LDS: a chunk's 16 dims are two 16-byte pieces
-      const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
-      if (tg == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int h = 0; h < QW; ++h)
-            qs[((g * CPL) * LPR + c) * QW + h] =
-                *(const uint4*)(qrow + (int64_t)g * D + c * VEC + h * 8);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      return;
-    }
-    const T* qrow = (const T*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
-    if (tg == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          uint4 v = *(const uint4*)(qrow + (int64_t)g * D + (c + k * LPR) * VEC);
-          if constexpr (!BF16) {
-            v.x = __float_as_uint(__uint_as_float(v.x) * a.scale_log2);
-            v.y = __float_as_uint(__uint_as_float(v.y) * a.scale_log2);
-            v.z = __float_as_uint(__uint_as_float(v.z) * a.scale_log2);
-            v.w = __float_as_uint(__uint_as_float(v.w) * a.scale_log2);
-          }
-          qs[(g * CPL + k) * LPR + c] = v;
-        }
-    }
-    // the wave's own LDS writes must land before its reads (no other wave
-    // touches this region)
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  }
-
-  __device__ void reset() {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      m_run[g] = -INFINITY;
-      l_run[g] = 0.f;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[g][k][e] = 0.f;
-    }
-  }
-
-  // Physical block of each load instruction of the tile at token t0 of the
-  // sequence whose table row is bt (keys < end).  Rows are clamped to end-1,
-  // so a tile past the end still addresses a written row.
-  __device__ void lookup(const int32_t* bt, int t0, int end, int (&ph)[NI]) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      if constexpr (UNIFORM) {
-        // scalar loads: a vector load here would be waited for together with
-        // the tile loads issued before it, draining the pipeline
-        ph[i] = bt[min(t0 + i * TPI, end - 1) >> a.log2_bs];
-      } else {
-        ph[i] = bt[min(t0 + i * TPI + tg, end - 1) >> a.log2_bs];
-      }
-    }
-  }
-
-  // Gather the K and V rows of the tile at t0 through the block table.
-  //
-  // UNIFORM: instruction i reads rows t0 + i*TPI .. +TPI-1 of the block that
-  // holds its first row (clamped to the range's last block), so the block
-  // base is wave-uniform (scalar registers) and every lane adds the same
-  // loop-invariant offset (tg rows down, its chunk across): no per-tile
-  // vector address arithmetic.  Rows at or past `end` stay inside that
-  // allocated block -- memory-safe -- and compute() masks them (their bytes
-  // may be unwritten NaN poison).  Otherwise each lane looks up its own row,
-  // clamped to end-1.
-  __device__ void issue(Tile& tl, int t0, int end, const int (&ph)[NI]) const {
-    const char* kp = (const char*)a.k_pool;
-    const char* vp = (const char*)a.v_pool;
-    if constexpr (UNIFORM) {
-      // buffer loads: descriptor of the block (scalar), row offset (scalar),
-      // lane offset (one loop-invariant vector register)
-      const uint32_t lane_off = (uint32_t)tg * row_bytes + lane_col;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int phys = min(max(ph[i], 0), nb_max);
-        const int64_t blk = phys * block_bytes;
-        const uint32_t row = (uint32_t)((t0 + i * TPI) & bs_mask) * row_bytes;
-        const __amdgpu_buffer_rsrc_t kr = buffer_rsrc(kp + blk, (uint32_t)block_bytes);
-        const __amdgpu_buffer_rsrc_t vr = buffer_rsrc(vp + blk, (uint32_t)block_bytes);
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.k[i][k] = buffer_load16_nt(kr, lane_off + k * kChunkStride, row);
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16_nt(vr, lane_off + k * kChunkStride, row);
-        if constexpr (FP8) {  // this lane's row: tg rows into the instruction's rows
-          const int64_t srow =
-              ((int64_t)phys << a.log2_bs) + ((t0 + i * TPI) & bs_mask) + tg;
-          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
-          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int tok = min(t0 + i * TPI + tg, end - 1);  // clamp rows past the end
-        const int phys = min(max(ph[i], 0), nb_max);
-        const uint32_t off = (uint32_t)(tok & bs_mask) * row_bytes + lane_col;
-        const char* kb = kp + phys * block_bytes + off;
-        const char* vb = vp + phys * block_bytes + off;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.k[i][k] = load16_nt(kb + k * kChunkStride);
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) tl.v[i][k] = load16_nt(vb + k * kChunkStride);
-        if constexpr (FP8) {
-          const int64_t srow = ((int64_t)phys << a.log2_bs) + (tok & bs_mask);
-          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
-          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
-        }
-      }
-    }
-  }
-
-  // Fold the tile at t0 (keys < end) into the running softmax state.
-  __device__ void compute(const Tile& tl, int t0, int end) {
-    // ---- scores: partial dots over the lane's chunks, then sum the row -----
-    float s[NI][G];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[i][g] = 0.f;
-    if constexpr (QREG) {  // each chunk of 16 codes converted once, dotted with every head
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float kf[16];
-        fp8x16_to_f32(tl.k[i][0], kf);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) d = fmaf(qf[g][e], kf[e], d);
-          s[i][g] = d;
-        }
-      }
-    } else if constexpr (FP8) {  // query from LDS, one head at a time
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const uint4 q0 = qs[((g * CPL) * LPR + c) * QW];
-        const uint4 q1 = qs[((g * CPL) * LPR + c) * QW + 1];
-        const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        float qg[16];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qg[2 * e] = bf16_lo(qw[e]);
-          qg[2 * e + 1] = bf16_hi(qw[e]);
-        }
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          float kf[16];
-          fp8x16_to_f32(tl.k[i][0], kf);
-          float d = 0.f;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) d = fmaf(qg[e], kf[e], d);
-          s[i][g] = d;
-        }
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G && !FP8; ++g) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const uint4 qv = qs[(g * CPL + k) * LPR + c];
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          float d = s[i][g];
-          if constexpr (BF16) {
-            d = dot2_bf16(qv.x, tl.k[i][k].x, d);
-            d = dot2_bf16(qv.y, tl.k[i][k].y, d);
-            d = dot2_bf16(qv.z, tl.k[i][k].z, d);
-            d = dot2_bf16(qv.w, tl.k[i][k].w, d);
-          } else {
-            d = fmaf(__uint_as_float(qv.x), __uint_as_float(tl.k[i][k].x), d);
-            d = fmaf(__uint_as_float(qv.y), __uint_as_float(tl.k[i][k].y), d);
-            d = fmaf(__uint_as_float(qv.z), __uint_as_float(tl.k[i][k].z), d);
-            d = fmaf(__uint_as_float(qv.w), __uint_as_float(tl.k[i][k].w), d);
-          }
-          s[i][g] = d;
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[i][g] = reduce_levels<0, LOG_LPR>(s[i][g], OpSum());
-    if constexpr (FP8) {  // the row's K scale (rows past the end are selected away below)
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[i][g] *= tl.ks[i];
-    }
-    const bool tail = t0 + TT > end;
-    if (tail) {  // rows past the end get probability 0
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const bool valid = (t0 + i * TPI + tg) < end;
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[i][g] = valid ? s[i][g] : -INFINITY;
-      }
-    }
-
-    // ---- online softmax (log2 domain), lazily rescaled ------------------------
-    float mt[G];
-    bool move = false;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = s[0][g];
-#pragma unroll
-      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[i][g]);
-      mt[g] = reduce_groups<LOG_LPR>(mx, OpMax()) * qk_scale;
-      move |= mt[g] > m_run[g] + kLazy;
-    }
-    if (__builtin_amdgcn_readfirstlane((int)move)) {  // same on every lane: make it scalar
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float m_new = fmaxf(m_run[g], mt[g]);
-        const float alpha = fast_exp2(m_run[g] - m_new);
-        m_run[g] = m_new;
-        l_run[g] *= alpha;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[g][k][e] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = fast_exp2(fmaf(s[i][g], qk_scale, -m_run[g]));
-        l_run[g] += p;
-        s[i][g] = p;
-      }
-    }
-
-    // ---- PV --------------------------------------------------------------------
-    if constexpr (FP8) {  // p * (code * scale): the row's V scale goes into p
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float vsc = tl.vs[i];
-        const bool valid = !(UNIFORM && tail) || (t0 + i * TPI + tg) < end;
-        vsc = valid ? vsc : 0.f;  // masked rows may hold NaN poison: select, never multiply
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          float vf[16];
-          fp8x16_to_f32(tl.v[i][k], vf);
-#pragma unroll
-          for (int e = 0; e < 16; ++e) vf[e] = valid ? vf[e] : 0.f;
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float pv = s[i][g] * vsc;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[g][k][e] = fmaf(pv, vf[e], acc[g][k][e]);
-          }
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        float v[VEC];
-        if constexpr (BF16) {
-          v[0] = bf16_lo(tl.v[i][k].x); v[1] = bf16_hi(tl.v[i][k].x);
-          v[2] = bf16_lo(tl.v[i][k].y); v[3] = bf16_hi(tl.v[i][k].y);
-          v[4] = bf16_lo(tl.v[i][k].z); v[5] = bf16_hi(tl.v[i][k].z);
-          v[6] = bf16_lo(tl.v[i][k].w); v[7] = bf16_hi(tl.v[i][k].w);
-        } else {
-          v[0] = __uint_as_float(tl.v[i][k].x); v[1] = __uint_as_float(tl.v[i][k].y);
-          v[2] = __uint_as_float(tl.v[i][k].z); v[3] = __uint_as_float(tl.v[i][k].w);
-        }
-        if (UNIFORM && tail) {  // masked rows may hold NaN poison: select, never multiply
-          const bool valid = (t0 + i * TPI + tg) < end;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) v[e] = valid ? v[e] : 0.f;
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[g][k][e] = fmaf(s[i][g], v[e], acc[g][k][e]);
-      }
-    }
-  }
-
-  // Fold the keys [start, end) of the sequence with table row bt, pipelined:
-  // the loads of tile t+1 are in flight while tile t is computed (two register
-  // tiles).  Loads are issued unconditionally -- past the end they re-read the
-  // clamped last row -- so each compute waits for exactly one older tile.
-  // Requires start < end.
-  __device__ void run(const int32_t* bt, int start, int end) {
-    int ph[NI];
-    lookup(bt, start, end, ph);
-    Tile ta, tb;
-    issue(ta, start, end, ph);
-    lookup(bt, start + TT, end, ph);
-    for (int t0 = start;;) {
-      issue(tb, t0 + TT, end, ph);
-      lookup(bt, t0 + 2 * TT, end, ph);
-      compute(ta, t0, end);
-      t0 += TT;
-      if (t0 >= end) break;
-      issue(ta, t0 + TT, end, ph);
-      lookup(bt, t0 + 2 * TT, end, ph);
-      compute(tb, t0, end);
-      t0 += TT;
-      if (t0 >= end) break;
-    }
-  }
-
-  // Sum the token groups: afterwards lanes with tg == 0 hold the full acc of
-  // their chunks and every lane the full l.
-  __device__ void combine(float (&l)[G]) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      l[g] = reduce_groups<LOG_LPR>(l_run[g], OpSum());
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[g][k][e] = reduce_groups<LOG_LPR>(acc[g][k][e], OpSum());
-    }
-  }
-
-  // Normalised output of query j (dtype T) -- after combine().
-  __device__ void store_out(void* out, int j, const float (&l)[G]) const {
-    if (tg != 0) return;
-    if constexpr (FP8) {  // bf16 output, 16 dims a chunk
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float inv = 1.f / l[g];
-        uint16_t* o = (uint16_t*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D;
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          const int col = (c + k * LPR) * VEC;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float* x = &acc[g][k][8 * h];
-            uint4 w;
-            w.x = pack_bf16x2(x[0] * inv, x[1] * inv);
-            w.y = pack_bf16x2(x[2] * inv, x[3] * inv);
-            w.z = pack_bf16x2(x[4] * inv, x[5] * inv);
-            w.w = pack_bf16x2(x[6] * inv, x[7] * inv);
-            *(uint4*)(o + col + 8 * h) = w;
-          }
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float inv = 1.f / l[g];
-      T* o = (T*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int col = (c + k * LPR) * VEC;
-        if constexpr (BF16) {
-          uint4 w;
-          w.x = pack_bf16x2(acc[g][k][0] * inv, acc[g][k][1] * inv);
-          w.y = pack_bf16x2(acc[g][k][2] * inv, acc[g][k][3] * inv);
-          w.z = pack_bf16x2(acc[g][k][4] * inv, acc[g][k][5] * inv);
-          w.w = pack_bf16x2(acc[g][k][6] * inv, acc[g][k][7] * inv);
-          *(uint4*)(o + col) = w;
-        } else {
-          *(float4*)(o + col) = make_float4(acc[g][k][0] * inv, acc[g][k][1] * inv,
-                                            acc[g][k][2] * inv, acc[g][k][3] * inv);
-        }
-      }
-    }
-  }
-
-  // Partial (o, lse) of head h = kvh*G + g at o_row(h) / lse_at(h) -- after combine().
-  template <class ORow, class LseAt>
-  __device__ void store_partial(ORow o_row, LseAt lse_at, const float (&l)[G]) const {
-    if (tg != 0) return;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int h = kvh * G + g;
-      const float inv = 1.f / l[g];
-      float* po = o_row(h);
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        const int col = (c + k * LPR) * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-          *(float4*)(po + col + e) = make_float4(acc[g][k][e] * inv, acc[g][k][e + 1] * inv,
-                                                 acc[g][k][e + 2] * inv, acc[g][k][e + 3] * inv);
-      }
-      if (c == 0) *lse_at(h) = (m_run[g] + __log2f(l[g])) * kLn2;
-    }
-  }
-
-  __device__ void store_zero(void* out, int j) const {
-    if (tg != 0) return;
-    if constexpr (FP8) {  // bf16 output
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int k = 0; k < CPL; ++k)
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            *(uint4*)((uint16_t*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D +
-                      (c + k * LPR) * VEC + 8 * h) = make_uint4(0, 0, 0, 0);
-      return;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int k = 0; k < CPL; ++k)
-        *(uint4*)((T*)out + ((int64_t)j * a.num_q_heads + kvh * G + g) * D +
-                  (c + k * LPR) * VEC) = make_uint4(0, 0, 0, 0);
-  }
-};
-
-// Query token j -> (sequence, number of query tokens of that sequence, first
-// query token of the sequence), binary search over cu_q_lens.
-__device__ __forceinline__ void locate(const DecodeArgs& a, int j, int& b, int& q_len,
-                                       int& q_first) {
-  b = j;
-  q_first = j;
-  q_len = 1;
-  if (a.cu_q_lens != nullptr) {
-    int lo = 0, hi = a.num_seqs - 1;  // last b with cu[b] <= j
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cu_q_lens[mid] <= j) lo = mid; else hi = mid - 1;
-    }
-    b = lo;
-    q_first = a.cu_q_lens[b];
-    q_len = a.cu_q_lens[b + 1] - q_first;
-  }
-}
+using namespace wave;
 
 // ---------------------------------------------------------------------------
-// Grid kernel: blockIdx.x = query token * groups + KV-head group (groups vary
-// fastest, so the heads of one block are read at about the same time),
-// blockIdx.z = partition, dispatched last-first so that the long sequences'
-// tails start early.
+// Grid kernel (single pass, one query token per sequence): blockIdx.x =
+// sequence * groups + KV-head group (groups vary fastest, so the heads of one
+// block are read at about the same time).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, bool SPLIT, bool UNIFORM>
+template <typename T, int D, int G, bool UNIFORM>
 __global__ __launch_bounds__(kMaxWaves * kWave) void decode_kernel(
     DecodeArgs a, const int32_t* __restrict__ block_tables) {
   const int groups = a.num_kv_heads / a.waves_per_group;
-  const int j = blockIdx.x / groups;
+  const int b = blockIdx.x / groups;
   const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
-  const int part = (int)gridDim.z - 1 - (int)blockIdx.z;
-
-  int b, q_len, q_first;
-  locate(a, j, b, q_len, q_first);
   const int cap = a.max_blocks << a.log2_bs;
-  const int len = min(max(a.seq_lens[b], 0), cap);
-  const int key_end = len - q_len + (j - q_first) + 1;  // keys 0 .. position
-  int start = 0, end = key_end;
-  if constexpr (SPLIT) {
-    if (q_len > 1 && a.prefill_mfma) return;  // the MFMA prefill kernel takes these
-    start = part * a.partition_size;
-    end = min(key_end, start + a.partition_size);
-    if (start >= end) return;  // this partition holds no key
-  }
+  const int end = min(max(a.seq_lens[b], 0), cap);  // keys 0 .. len-1
   using W = WaveCtx<T, D, G, UNIFORM>;
   __shared__ uint4 q_lds[kMaxWaves][W::kQChunks];
   W w(a, kvh, q_lds[wave_id()]);
-  if constexpr (!SPLIT) {
-    if (end <= 0) {
-      w.store_zero(a.out, j);
-      return;
-    }
+  if (end <= 0) {
+    w.store_zero(a.out, b);
+    return;
   }
-  w.load_query(j);
+  w.load_query(b);
   w.reset();
-  w.run(block_tables + (int64_t)b * a.max_blocks, start, end);
+  w.run(block_tables + (int64_t)b * a.max_blocks, 0, end);
   float l[G];
   w.combine(l);
-  if constexpr (SPLIT) {
-    const int64_t base = (int64_t)j * a.num_q_heads;
-    w.store_partial(
-        [&](int h) { return a.part_o + ((base + h) * a.max_partitions + part) * D; },
-        [&](int h) { return a.part_lse + (base + h) * a.max_partitions + part; }, l);
-  } else {
-    w.store_out(a.out, j, l);
-  }
+  w.store_out(a.out, b, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -954,41 +338,27 @@ constexpr int tpi() {
 }
 
 template <typename T, int D, int G>
-pa_status launch_grid(const DecodeArgs& a, bool split, hipStream_t stream) {
+pa_status launch_grid(const DecodeArgs& a, hipStream_t stream) {
   const int groups = a.num_kv_heads / a.waves_per_group;
-  const dim3 grid((uint32_t)((int64_t)a.num_q_tokens * groups), 1, split ? a.max_partitions : 1);
+  const dim3 grid((uint32_t)((int64_t)a.num_seqs * groups));
   const dim3 block(a.waves_per_group * kWave);
-  const bool uniform = (1 << a.log2_bs) >= tpi<T, D, G>();
-  if (split) {
-    if (uniform)
-      hipLaunchKernelGGL((decode_kernel<T, D, G, true, true>), grid, block, 0, stream, a,
-                         a.block_tables);
-    else
-      hipLaunchKernelGGL((decode_kernel<T, D, G, true, false>), grid, block, 0, stream, a,
-                         a.block_tables);
-  } else {
-    if (uniform)
-      hipLaunchKernelGGL((decode_kernel<T, D, G, false, true>), grid, block, 0, stream, a,
-                         a.block_tables);
-    else
-      hipLaunchKernelGGL((decode_kernel<T, D, G, false, false>), grid, block, 0, stream, a,
-                         a.block_tables);
-  }
+  if ((1 << a.log2_bs) >= tpi<T, D, G>())
+    hipLaunchKernelGGL((decode_kernel<T, D, G, true>), grid, block, 0, stream, a,
+                       a.block_tables);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, D, G, false>), grid, block, 0, stream, a,
+                       a.block_tables);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 template <typename T, int D, int G>
-pa_status stream_per_cu(const DecodeArgs& a, int* per_cu) {
+pa_status stream_per_cu(const DecodeArgs& a, int dev, int* per_cu) {
   const size_t lds = stream_lds_bytes(a.num_seqs);
   const int threads = a.waves_per_group * kWave;
-  hipError_t e;
-  if ((1 << a.log2_bs) >= tpi<T, D, G>())
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        per_cu, decode_stream_kernel<T, D, G, true>, threads, lds);
-  else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        per_cu, decode_stream_kernel<T, D, G, false>, threads, lds);
-  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+  const void* k = (1 << a.log2_bs) >= tpi<T, D, G>()
+                      ? (const void*)decode_stream_kernel<T, D, G, true>
+                      : (const void*)decode_stream_kernel<T, D, G, false>;
+  return resident_per_cu(dev, k, threads, lds, per_cu);
 }
 
 template <typename T, int D, int G>
@@ -1009,56 +379,20 @@ pa_status launch_stream(const DecodeArgs& a, const StreamArgs& s, hipStream_t st
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
-// (dtype, head_dim, G) -> template instance: f.template operator()<T, D, G>().
-template <class F>
-pa_status dispatch(const DecodeArgs& a, F&& f) {
-  const int g = a.num_q_heads / a.num_kv_heads;
-  auto by_g = [&](auto t, auto d) -> pa_status {
-    using T = decltype(t);
-    constexpr int Dv = decltype(d)::value;
-    switch (g) {
-      case 1: return f.template operator()<T, Dv, 1>();
-      case 2: return f.template operator()<T, Dv, 2>();
-      case 4: return f.template operator()<T, Dv, 4>();
-      case 8: return f.template operator()<T, Dv, 8>();
-      default: return PA_ERR_UNSUPPORTED;
-    }
-  };
-  auto by_d = [&](auto t) -> pa_status {
-    switch (a.head_dim) {
-      case 32:
-        // fp8 rows of 32 codes would put 32 tokens in one load instruction,
-        // more than the 16-token alignment of partitions and slices
-        if constexpr (sizeof(decltype(t)) == 1) return PA_ERR_UNSUPPORTED;
-        else return by_g(t, std::integral_constant<int, 32>());
-      case 64: return by_g(t, std::integral_constant<int, 64>());
-      case 128: return by_g(t, std::integral_constant<int, 128>());
-      case 256: return by_g(t, std::integral_constant<int, 256>());
-      default: return PA_ERR_UNSUPPORTED;
-    }
-  };
-  if (a.dtype == PA_BF16) return by_d(uint16_t());
-  if (a.dtype == PA_F32) return by_d(float());
-  if (a.dtype == PA_FP8) return by_d(uint8_t());
-  return PA_ERR_UNSUPPORTED;
-}
-
 }  // namespace
 
 size_t stream_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
 
-pa_status launch_decode(const DecodeArgs& a, bool split, void* stream) {
+pa_status launch_decode(const DecodeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  return dispatch(a, [&]<typename T, int D, int G>() { return launch_grid<T, D, G>(a, split, s); });
+  return dispatch(a, [&]<typename T, int D, int G>() { return launch_grid<T, D, G>(a, s); });
 }
 
 pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices) {
   int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return PA_ERR_HIP;
-  const pa_status st =
-      dispatch(a, [&]<typename T, int D, int G>() { return stream_per_cu<T, D, G>(a, &per_cu); });
+  if (current_device(&dev) != PA_OK || device_cus(dev, &cus) != PA_OK) return PA_ERR_HIP;
+  const pa_status st = dispatch(
+      a, [&]<typename T, int D, int G>() { return stream_per_cu<T, D, G>(a, dev, &per_cu); });
   if (st != PA_OK) return st;
   if (per_cu < 1) return PA_ERR_UNSUPPORTED;
   // slices = workgroups resident at once, shared out among the KV-head groups

@@ -188,6 +188,17 @@ __device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Masking selects done on bit patterns.  The library is built with relaxed
+// NaN handling (so that fmaxf needs no quieting); a select between integers
+// cannot be rewritten by any floating-point assumption, so a masked row's
+// NaN-poisoned bytes are replaced before they reach any arithmetic.
+__device__ __forceinline__ float select_bits(bool keep, float x, float other) {
+  return __uint_as_float(keep ? __float_as_uint(x) : __float_as_uint(other));
+}
+__device__ __forceinline__ uint4 mask_words(bool keep, uint4 w) {
+  return keep ? w : make_uint4(0u, 0u, 0u, 0u);
+}
+
 // 2^x on the transcendental unit; exact 0 for x = -inf.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

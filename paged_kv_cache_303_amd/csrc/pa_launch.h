@@ -39,7 +39,7 @@ struct DecodeArgs {
   int32_t partition_size;      // tokens per partition (split) or 0 (single pass)
   int32_t max_partitions;
   int32_t waves_per_group;     // KV heads (= waves) per workgroup
-  int32_t prefill_mfma;        // split: multi-query sequences go to the MFMA prefill kernel
+  int32_t* queue;              // split: work-queue counters in the caller's workspace
 };
 
 struct ReduceArgs {
@@ -73,17 +73,28 @@ struct StreamArgs {
 constexpr int32_t kStreamMaxSeqs = 4096;
 size_t stream_lds_bytes(int32_t num_seqs);
 
+// Cached device facts (pa_devinfo.cpp): the calling thread's current device,
+// its compute-unit count, and how many workgroups of `kernel` (threads per
+// workgroup, dynamic LDS bytes) one compute unit holds at once.
+pa_status current_device(int* dev);
+pa_status device_cus(int dev, int* cus);
+pa_status resident_per_cu(int dev, const void* kernel, int threads, size_t lds, int* per_cu);
+
 // Returns PA_OK, PA_ERR_UNSUPPORTED (no instance for the shape) or PA_ERR_HIP.
-pa_status launch_decode(const DecodeArgs& a, bool split, void* stream);
+// Single-pass grid decode (one workgroup per sequence and KV-head group).
+pa_status launch_decode(const DecodeArgs& a, void* stream);
 // Number of slices = workgroups of the streaming kernel resident on the
 // current device at once / KV-head groups.
 pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices);
 pa_status launch_decode_stream(const DecodeArgs& a, const StreamArgs& s, void* stream);
+// Split first pass: one persistent launch over a work list of decode
+// partitions and (bf16, head_dim <= 128) matrix-core prefill row tiles;
+// writes partition p of every single-query sequence's query and partition 0
+// (all keys) of every query of a multi-query sequence.
+constexpr int32_t kSplitMaxSeqs = 8192;  // sequences per launch (LDS prefix sums)
+constexpr int32_t kSplitQueueInts = 16;  // work-queue counters in the workspace
+pa_status launch_split(const DecodeArgs& a, void* stream);
 pa_status launch_reduce(const ReduceArgs& a, void* stream);
-// Chunked-prefill tile on the matrix cores (bf16; cu_q_lens given): writes
-// partition 0 of every query token of the sequences with q_len > 1.
-bool prefill_mfma_supported(const DecodeArgs& a);
-pa_status launch_prefill_mfma(const DecodeArgs& a, void* stream);
 pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,
                           const void* v_new, const int32_t* slots, int32_t num_tokens,
                           void* stream);

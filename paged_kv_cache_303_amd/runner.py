@@ -106,9 +106,17 @@ def replay(w, device, poison: bool = True, tokens_on_device=None):
     }
 
 
-def attention(w, st, partition_size=None):
+def split_workspace(w, st, partition_size=None):
+    """A zeroed split workspace sized for the workload's queries."""
+    p = w.partition_size if partition_size is None else partition_size
+    maxp = binding.max_partitions_for(w.max_blocks, w.block_size, p, st["cu_q_lens"] is not None)
+    q = st["q"]
+    return binding.SplitWorkspace(q.shape[0], q.shape[1], q.shape[2], maxp, q.device)
+
+
+def attention(w, st, partition_size=None, workspace=None, out=None):
     """Split pass + reduce over the workload's queries (device output)."""
     p = w.partition_size if partition_size is None else partition_size
     return binding.paged_attention(st["q"], st["k_pool"], st["v_pool"], st["block_tables"],
                                    st["seq_lens"], w.scale, partition_size=p,
-                                   cu_q_lens=st["cu_q_lens"])
+                                   cu_q_lens=st["cu_q_lens"], workspace=workspace, out=out)

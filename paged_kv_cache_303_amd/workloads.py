@@ -94,8 +94,10 @@ class Workload:
 
     @property
     def max_partitions(self) -> int:
+        """Partition slots per query for the split layout: enough for the longest
+        table, and two for workloads with prefill chunks."""
         cap = self.max_blocks * self.block_size
-        return max(1, -(-cap // self.partition_size))
+        return max(2 if self.cu_q_lens is not None else 1, -(-cap // self.partition_size))
 
     @property
     def cu_q_lens(self):

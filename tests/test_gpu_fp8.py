@@ -62,7 +62,7 @@ def _oracle_fp8(w, st_o):
 
 def _run(pa, w, tokens=None):
     binding, runner, dev = pa
-    assert w.dtype == wl.BF16 and w.cu_q_lens is None
+    assert w.dtype == wl.BF16
     print(f"[case] fp8 {w.name} B={len(w.decode_seqs)} heads={w.num_q_heads}/{w.num_kv_heads} "
           f"d={w.head_dim} bs={w.block_size}", flush=True)
     st = runner.replay(w, dev, poison=False)
@@ -76,16 +76,28 @@ def _run(pa, w, tokens=None):
         assert np.array_equal(gt.cpu().numpy(), ot), name
     for name, gt, ot in zip(("k scales", "v scales"), g[2:], o[2:]):
         assert np.array_equal(gt.cpu().numpy().view(np.uint32), ot.view(np.uint32)), name
-    ref = paged_attention(w.q, oq.dequantize(o[0], o[2]), oq.dequantize(o[1], o[3]),
-                          st_o["block_tables"], st_o["seq_lens"], w.scale, w.block_size,
-                          tokens=tokens)
+    # the oracle reads the dequantized values of the blocks the tables use
+    # (a compact copy of those blocks, tables renumbered: the same rows)
+    tables = st_o["block_tables"]
+    used = np.unique(tables[tables >= 0])
+    renum = np.full(w.num_blocks, -1, np.int32)
+    renum[used] = np.arange(len(used), dtype=np.int32)
+    ctab = np.where(tables >= 0, renum[np.maximum(tables, 0)], -1)
+    ref = paged_attention(w.q, oq.dequantize(o[0][used], o[2][used]),
+                          oq.dequantize(o[1][used], o[3][used]), ctab, st_o["seq_lens"],
+                          w.scale, w.block_size, cu_q_lens=w.cu_q_lens, tokens=tokens)
     args = (st["q"], g[0], g[1], g[2], g[3], st["block_tables"], st["seq_lens"], w.scale)
-    stats = {"grid": check_attention(binding.decode_fp8(*args), ref, "bf16", tokens,
-                                     f"{w.name} fp8 grid")}
-    ws = binding.decode_workspace(g[0], len(w.seq_lens), w.num_q_heads)
-    if ws is not None:
-        stats["balanced"] = check_attention(binding.decode_fp8(*args, workspace=ws), ref, "bf16",
-                                            tokens, f"{w.name} fp8 balanced")
+    stats = {}
+    if w.cu_q_lens is None:
+        stats["grid"] = check_attention(binding.decode_fp8(*args), ref, "bf16", tokens,
+                                        f"{w.name} fp8 grid")
+        ws = binding.decode_workspace(g[0], len(w.seq_lens), w.num_q_heads)
+        if ws is not None:
+            stats["balanced"] = check_attention(binding.decode_fp8(*args, workspace=ws), ref,
+                                                "bf16", tokens, f"{w.name} fp8 balanced")
+    out = binding.paged_attention_fp8(*args, partition_size=w.partition_size,
+                                      cu_q_lens=st["cu_q_lens"])
+    stats["split"] = check_attention(out, ref, "bf16", tokens, f"{w.name} fp8 split")
     print(f"[parity] {w.name} fp8: " + ", ".join(f"{k} max_err={v[0]:.2e} rel={v[1]:.2e}"
                                                   for k, v in stats.items()), flush=True)
     return stats
@@ -119,6 +131,31 @@ def test_fp8_gqa_batch(pa):
     _run(pa, w)
 
 
+def test_fp8_gqa_decode_full(pa):
+    """The batch-256 GQA workload (the size the FP8 throughput is measured
+    at) from an e4m3 cache: every query row, grid, balanced and split paths."""
+    w = wl.gqa_decode()
+    w.name = "fp8_gqa_b256"
+    _run(pa, w)
+
+
+def test_fp8_split_with_prefill(pa):
+    """Split path over e4m3 pools: decode partitions and prefill chunks (on the
+    vector units for fp8) in one launch, partitions not a multiple of the tile."""
+    w = wl.custom_decode(17, [9, 64, 5, 300, 77, 1000], num_blocks=256, block_size=16,
+                         num_q_heads=8, num_kv_heads=2, head_dim=128, dtype=wl.BF16,
+                         q_lens=[1, 23, 5, 1, 40, 1], partition_size=48, name="fp8_split_prefill")
+    _run(pa, w)
+
+
+def test_fp8_long_context(pa):
+    """The long-context workload (8 x 32768 decode + a 512-token causal chunk,
+    block size 32) from an e4m3 cache, every query row."""
+    w = wl.long_context()
+    w.name = "fp8_long_context"
+    _run(pa, w)
+
+
 def test_fp8_zero_rows_and_empty_sequence(pa):
     binding, runner, dev = pa
     w = wl.custom_decode(7, [5, 3, 9], num_blocks=16, block_size=4, num_q_heads=4,
@@ -140,9 +177,11 @@ def test_fp8_zero_rows_and_empty_sequence(pa):
         assert torch.isfinite(out.float()).all()
 
 
-def test_fp8_copy_blocks(pa):
+@pytest.mark.parametrize("shape", [(8, 16, 2, 64), (8, 1, 2, 64), (8, 2, 1, 64), (8, 1, 1, 64)])
+def test_fp8_copy_blocks(pa, shape):
+    """Codes and scales copied bit for bit; scale blocks of 8, 8 and 4 bytes
+    (not whole 16-byte units) included."""
     binding, runner, dev = pa
-    shape = (8, 16, 2, 64)
     gen = torch.Generator().manual_seed(0)
     kc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)
     vc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)

@@ -4,8 +4,8 @@ Every workload is replayed twice from the same seeded inputs -- through the
 C++ block pool and the GPU kernels, and through the oracle allocator and the
 oracle cache writes -- then compared: block tables, slot mappings,
 copy-on-write pairs and pool bytes bit for bit, attention outputs within the
-tolerances of tests/parity.py.  Full-size workloads check a sample of query
-tokens (the longest and shortest sequences included) against the oracle.
+tolerances of tests/parity.py.  Every query row of every workload, the
+full-size ones included, is checked against the oracle.
 """
 
 import numpy as np
@@ -40,20 +40,6 @@ def _both(pa, w, poison=True):
     assert pools_equal_bits(st_p["k_pool"], st_o["k_pool"])
     assert pools_equal_bits(st_p["v_pool"], st_o["v_pool"])
     return st_p, st_o
-
-
-def _sample_tokens(w, n=24, seed=0):
-    """Query tokens to check: the longest/shortest sequences plus a random sample."""
-    positions = []
-    start = 0
-    for i, ql in enumerate(w.q_lens):
-        positions += [(w.seq_lens[i], start + k) for k in range(ql)]
-        start += ql
-    order = sorted(range(len(positions)), key=lambda k: positions[k][0])
-    pick = set(order[:4] + order[-6:])
-    rng = np.random.default_rng(seed)
-    pick |= set(rng.choice(len(positions), size=min(n, len(positions)), replace=False).tolist())
-    return sorted(positions[k][1] for k in pick)
 
 
 def _check_all_paths(pa, w, st_p, st_o, tokens=None, partitions=(None,)):
@@ -157,11 +143,11 @@ def test_prefill_partials_match_oracle(pa, dtype):
                          q_lens=[100, 1, 3, 80], partition_size=32, name="prefill_partials")
     st_p, st_o = _both(pa, w)
     o_ref, lse_ref, nparts = orun.partials(w, st_o)
-    part_o, part_lse = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
-                                            st_p["block_tables"], st_p["seq_lens"], w.scale,
-                                            partition_size=w.partition_size,
-                                            cu_q_lens=st_p["cu_q_lens"])
-    po, pl = to_f64(part_o), to_f64(part_lse)
+    ws = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
+                              st_p["block_tables"], st_p["seq_lens"], w.scale,
+                              partition_size=w.partition_size, cu_q_lens=st_p["cu_q_lens"])
+    po, pl = to_f64(ws.part_o), to_f64(ws.part_lse)
+    assert max(nparts) >= 2  # the chunks' queries are split at half their context
     for j, n in enumerate(nparts):
         if dtype == wl.F32:
             np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=1e-5)
@@ -189,9 +175,10 @@ def test_gqa_decode_small_f32(pa):
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_gqa_decode_full(pa, dtype):
+    """The batch-256 GQA workload, every query row, every path."""
     w = wl.gqa_decode(dtype=dtype)
     st_p, st_o = _both(pa, w)
-    _check_all_paths(pa, w, st_p, st_o, tokens=_sample_tokens(w, n=40))
+    _check_all_paths(pa, w, st_p, st_o)
 
 
 def test_shared_prefix_full(pa):
@@ -208,9 +195,11 @@ def test_shared_prefix_full(pa):
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
 def test_long_context_full(pa, dtype):
+    """8 x 32768 decode + a 512-token causal chunk in one split launch: every
+    query row (the chunk's 512 included) against the oracle."""
     w = wl.long_context(dtype=dtype)
     st_p, st_o = _both(pa, w)
-    _check_all_paths(pa, w, st_p, st_o, tokens=_sample_tokens(w, n=24))
+    _check_all_paths(pa, w, st_p, st_o)
 
 
 # --- partials, edge cases, determinism ------------------------------------------------------
@@ -223,10 +212,10 @@ def test_split_partials_match_oracle(pa, dtype):
                          dtype=dtype, partition_size=64, name="partials")
     st_p, st_o = _both(pa, w)
     o_ref, lse_ref, nparts = orun.partials(w, st_o)
-    part_o, part_lse = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
-                                            st_p["block_tables"], st_p["seq_lens"], w.scale,
-                                            partition_size=w.partition_size)
-    po, pl = to_f64(part_o), to_f64(part_lse)
+    ws = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
+                              st_p["block_tables"], st_p["seq_lens"], w.scale,
+                              partition_size=w.partition_size)
+    po, pl = to_f64(ws.part_o), to_f64(ws.part_lse)
     tol = 1e-5 if dtype == wl.F32 else 1e-4
     for j, n in enumerate(nparts):
         np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=tol)
@@ -330,6 +319,32 @@ def test_copy_blocks_exact(pa):
         assert torch.equal(k[d], k0[s]) and torch.equal(v[d], v0[s])
     for b in [0, 1, 2, 3, 4, 5, 6]:
         assert torch.equal(k[b], k0[b]) and torch.equal(v[b], v0[b])
+
+
+def test_split_workspace_reuse(pa):
+    """One workspace across calls: the work-queue counters the split launch
+    leaves behind must be zero again, so each call covers every item.  A
+    small call (fewer items than workgroups) and a large one, alternating,
+    each against the oracle, with the counters read back after each."""
+    binding, runner, dev = pa
+    small = wl.custom_decode(31, [1, 40, 3], num_blocks=512, block_size=16, num_q_heads=8,
+                             num_kv_heads=2, head_dim=128, dtype=wl.BF16, q_lens=[1, 9, 1],
+                             partition_size=32, name="reuse_small")
+    big = wl.custom_decode(32, [700, 90, 1500], num_blocks=512, block_size=16, num_q_heads=8,
+                           num_kv_heads=2, head_dim=128, dtype=wl.BF16, q_lens=[1, 9, 1],
+                           partition_size=32, name="reuse_big")
+    ws = binding.SplitWorkspace(11, 8, 128, 64, dev)
+    ctrl = ws.buffer[ws.layout.control_offset:ws.layout.control_offset + 256]
+    for w in (small, big, small, big):
+        st_p, st_o = _both(pa, w)
+        ref = orun.attention(w, st_o)
+        out = binding.paged_attention(st_p["q"], st_p["k_pool"], st_p["v_pool"],
+                                      st_p["block_tables"], st_p["seq_lens"], w.scale,
+                                      partition_size=w.partition_size,
+                                      cu_q_lens=st_p["cu_q_lens"], workspace=ws)
+        check_attention(out, ref, w.dtype, what=f"{w.name} reused workspace")
+        torch.cuda.synchronize()
+        assert int(ctrl.sum()) == 0, "work-queue counters not returned to zero"
 
 
 def test_deterministic(pa):

@@ -190,13 +190,42 @@ def test_split_merge_equals_full_attention(partition):
 
 
 def test_split_causal_chunk_partials_merge():
-    w = wl.custom_decode(8, [40, 70], num_blocks=64, block_size=4, num_q_heads=4,
-                         num_kv_heads=1, head_dim=8, dtype=wl.F32, q_lens=[3, 33],
+    """Prefill chunks next to a decode query.  A chunk's query has two
+    partitions split at half the cached context in whole 32-key tiles (keys
+    [0, h) and [h, position]), or one when that half is empty; each summary is
+    checked against torch's SDPA on contiguous K/V (with an explicit causal
+    mask) and scipy's logsumexp of the visible scores.  The decode query keeps
+    its ceil(len / P) partitions."""
+    w = wl.custom_decode(8, [40, 70, 50, 20], num_blocks=64, block_size=4, num_q_heads=4,
+                         num_kv_heads=1, head_dim=8, dtype=wl.F32, q_lens=[3, 33, 1, 10],
                          partition_size=16)
     st = runner.replay(w)
     o, lse, nparts = runner.partials(w, st)
     merged, _ = oracle.merge_partials(o, lse, nparts)
     np.testing.assert_allclose(merged, runner.attention(w, st), rtol=0, atol=1e-12)
+    # split points by hand: contexts 37, 37, -, 10 -> 2 tiles -> h = 32; 1 tile -> h = 0
+    assert [oatt.prefill_split(n, ql) for n, ql in [(40, 3), (70, 33), (20, 10)]] == [32, 32, 0]
+    q = widen(w.q)
+    j0 = 0
+    for i, (k, v) in enumerate(contiguous_kv(w)):
+        ql, n = w.q_lens[i], w.seq_lens[i]
+        if ql == 1:
+            assert nparts[j0] == -(-n // w.partition_size)
+            j0 += 1
+            continue
+        h = {40: 32, 70: 32, 20: 0}[n]
+        assert (nparts[j0:j0 + ql] == (2 if h else 1)).all()
+        for t in range(ql):
+            key_end = n - ql + t + 1
+            bounds = [(0, h), (h, key_end)] if h else [(0, key_end)]
+            s = (q[j0 + t] @ k[:key_end, 0].T) * w.scale  # one KV head
+            for p, (lo, hi) in enumerate(bounds):
+                ref = sdpa(q[j0 + t:j0 + t + 1], k[lo:hi], v[lo:hi], w.scale)[0]
+                np.testing.assert_allclose(o[j0 + t, :, p], ref, rtol=0, atol=1e-12)
+                np.testing.assert_allclose(lse[j0 + t, :, p],
+                                           scipy.special.logsumexp(s[:, lo:hi], axis=1),
+                                           rtol=0, atol=1e-12)
+        j0 += ql
 
 
 # --- bfloat16 helpers against torch -------------------------------------------------
