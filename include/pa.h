@@ -130,6 +130,26 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                     float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* pa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without the workspace, and the same balanced decode, whose
+ * workspace is a library-owned device array of 8 MiB per device (held until
+ * the process ends).  The call itself allocates nothing.  The batch is cut
+ * into as many slices as the device holds workgroups at once, or as many as
+ * fit in the 8 MiB when fewer do (the same result, less parallel); sizes of
+ * which even one slice does not fit (num_q_heads * head_dim beyond about
+ * 8 Mi elements / 8) return PA_ERR_UNSUPPORTED; batches the balanced path
+ * does not take (more than 4096 sequences) run the single-pass kernels,
+ * which need no scratch.  Every call on one device
+ * shares that device's array: calls that overlap in time on one device (on
+ * different streams, or from different threads) race and must not be
+ * issued. */
+pa_status pa_decode_noalloc(const pa_kv_layout* layout, void* out, const void* q,
+                            const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            float scale, void* stream);
+
 /* Bytes of workspace pa_decode uses for these sizes on the current device
  * (0: the balanced path does not apply, e.g. more than 4096 sequences, and
  * the workspace is ignored). */

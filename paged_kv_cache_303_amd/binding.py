@@ -57,6 +57,7 @@ _SIGNATURES = {
     "pa_decode": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p,
                          ctypes.c_size_t, _p]),
     "pa_decode_workspace_size": (_i32, [_LAYOUT, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pa_decode_noalloc": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32, _p]),
     "pa_kv_write_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _p, _p, _i32, _p]),
     "pa_decode_fp8": (_i32, [_LAYOUT, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _f32,
                              _p, ctypes.c_size_t, _p]),
@@ -324,6 +325,22 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out=None, wo
     _check(lib().pa_decode(ctypes.byref(lay), _dev(out, "out", k_pool.dtype),
                            _dev(q, "q", k_pool.dtype), kp, vp, bt, mb, sl, b, hq, float(scale),
                            ws, ws_bytes, _stream()))
+    return out
+
+
+def decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, scale: float, out):
+    """``pa_decode_noalloc``: the balanced decode on the library's own scratch
+    (``out`` is required: this call allocates nothing)."""
+    lay, kp, vp = _pools(k_pool, v_pool)
+    if q.dim() != 3 or q.shape[2] != lay.head_dim:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    if out is None or out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    b, hq = int(q.shape[0]), int(q.shape[1])
+    bt, mb, sl = _tables(block_tables, seq_lens, b)
+    _check(lib().pa_decode_noalloc(ctypes.byref(lay), _dev(out, "out", k_pool.dtype),
+                                   _dev(q, "q", k_pool.dtype), kp, vp, bt, mb, sl, b, hq,
+                                   float(scale), _stream()))
     return out
 
 

@@ -146,6 +146,15 @@ struct StreamLayout {
   size_t total() const { return o_bytes + lse_bytes + cum_bytes; }
 };
 
+StreamLayout stream_layout_for(const pa::DecodeArgs& a, int32_t slices) {
+  StreamLayout sl;
+  sl.slices = slices;
+  sl.o_bytes = align256((size_t)slices * 2 * a.num_q_heads * a.head_dim * sizeof(float));
+  sl.lse_bytes = align256((size_t)slices * 2 * a.num_q_heads * sizeof(float));
+  sl.cum_bytes = align256((size_t)a.num_seqs * 4 * sizeof(int32_t));
+  return sl;
+}
+
 // Workspace of the balanced path for these arguments (slices = 0: the batch
 // is too large for it and the grid kernel runs instead).
 pa_status stream_layout(const pa::DecodeArgs& a, StreamLayout* sl) {
@@ -154,10 +163,7 @@ pa_status stream_layout(const pa::DecodeArgs& a, StreamLayout* sl) {
   int32_t slices = 0;
   const pa_status st = pa::stream_slices(a, &slices);
   if (st != PA_OK) return st;
-  sl->slices = slices;
-  sl->o_bytes = align256((size_t)slices * 2 * a.num_q_heads * a.head_dim * sizeof(float));
-  sl->lse_bytes = align256((size_t)slices * 2 * a.num_q_heads * sizeof(float));
-  sl->cum_bytes = align256((size_t)a.num_seqs * 4 * sizeof(int32_t));
+  *sl = stream_layout_for(a, slices);
   return PA_OK;
 }
 
@@ -222,9 +228,10 @@ pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
 
 }  // extern "C"
 
-// pa_decode / pa_decode_fp8 after their own argument checks.
+// pa_decode / pa_decode_fp8 / pa_decode_noalloc after their own argument
+// checks; max_slices > 0 caps the balanced path's slices (its workspace).
 static pa_status decode_launch(const char* what, pa::DecodeArgs& a, void* out, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               size_t workspace_bytes, void* stream, int32_t max_slices = 0) {
   if (a.num_seqs == 0) return PA_OK;
   if (!out) return fail(PA_ERR_INVALID_ARG, "%s: out is NULL", what);
   a.out = out;
@@ -232,6 +239,7 @@ static pa_status decode_launch(const char* what, pa::DecodeArgs& a, void* out, v
     StreamLayout sl;
     if (pa_status st = stream_layout(a, &sl))
       return fail(st, "%s: cannot query the device occupancy", what);
+    if (max_slices > 0 && sl.slices > max_slices) sl = stream_layout_for(a, max_slices);
     if (sl.slices > 0) {
       if (workspace_bytes < sl.total())
         return fail(PA_ERR_INVALID_ARG, "%s: workspace of %zu bytes < %zu needed", what,
@@ -265,6 +273,40 @@ pa_status pa_decode(const pa_kv_layout* layout, void* out, const void* q, const 
   if (layout->dtype == PA_FP8)
     return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools need their scales: use pa_decode_fp8", what);
   return decode_launch(what, a, out, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_noalloc(const pa_kv_layout* layout, void* out, const void* q,
+                            const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_q_heads, float scale, void* stream) {
+  const char* what = "pa_decode_noalloc";
+  pa::DecodeArgs a;
+  if (pa_status st = fill_decode_args(what, layout, q, k_pool, v_pool, block_tables,
+                                      max_blocks_per_seq, seq_lens, num_seqs, num_q_heads, scale,
+                                      &a))
+    return st;
+  if (layout->dtype == PA_FP8)
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 pools are decoded by pa_decode_fp8", what);
+  if (num_seqs == 0) return PA_OK;
+  StreamLayout sl;
+  if (pa_status st = stream_layout(a, &sl))
+    return fail(st, "%s: cannot query the device occupancy", what);
+  if (sl.slices == 0)  // the balanced path does not apply: the grid kernel needs no scratch
+    return decode_launch(what, a, out, nullptr, 0, stream);
+  // as many slices as the device holds at once, or as fit in the scratch
+  int32_t slices = sl.slices;
+  while (slices > 0 && stream_layout_for(a, slices).total() > pa::kScratchBytes)
+    slices = stream_layout_for(a, slices).total() / 2 > pa::kScratchBytes ? slices / 2
+                                                                            : slices - 1;
+  if (slices < 1)
+    return fail(PA_ERR_UNSUPPORTED,
+                "%s: one slice of these sizes needs %zu bytes of scratch, more than the "
+                "library's %zu; use pa_decode with a workspace",
+                what, stream_layout_for(a, 1).total(), pa::kScratchBytes);
+  void* scratch = nullptr;
+  if (pa::scratch_buffer(&scratch) != PA_OK)
+    return fail(PA_ERR_HIP, "%s: cannot find the scratch array on this device", what);
+  return decode_launch(what, a, out, scratch, pa::kScratchBytes, stream, slices);
 }
 
 pa_status pa_decode_fp8(const pa_kv_layout* layout, void* out, const void* q,

@@ -33,6 +33,8 @@
 //   * Software pipeline: the next tile's loads are in flight while the current
 //     tile is computed.  Rows past a range's end are clamped to its last row
 //     and get probability exactly 0, so NaN-poisoned tails never reach sums.
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "pa_wave.h"
@@ -382,6 +384,31 @@ pa_status launch_stream(const DecodeArgs& a, const StreamArgs& s, hipStream_t st
 }  // namespace
 
 size_t stream_lds_bytes(int32_t num_seqs) { return (size_t)(2 * num_seqs + 1) * sizeof(int); }
+
+// Scratch of pa_decode_noalloc: the balanced decode's workspace (partial rows,
+// partial lse values, per-sequence slice records) in a library-owned array,
+// one copy per device, held until the process ends.  Nothing in it has to
+// start at zero: the streaming kernel writes every entry the merge reads.
+// In host code `scratch` only names the symbol; its device address on the
+// current device comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+pa_status scratch_buffer(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> by_device;
+  int dev = 0;
+  if (current_device(&dev) != PA_OK) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it == by_device.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    it = by_device.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return PA_OK;
+}
 
 pa_status launch_decode(const DecodeArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;

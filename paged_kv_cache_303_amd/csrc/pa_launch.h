@@ -87,6 +87,10 @@ pa_status launch_decode(const DecodeArgs& a, void* stream);
 // current device at once / KV-head groups.
 pa_status stream_slices(const DecodeArgs& a, int32_t* num_slices);
 pa_status launch_decode_stream(const DecodeArgs& a, const StreamArgs& s, void* stream);
+// The library's own device scratch for the balanced decode (pa_decode_noalloc):
+// kScratchBytes on every device, its address on the current device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+pa_status scratch_buffer(void** ptr);
 // Split first pass: one persistent launch over a work list of decode
 // partitions and (bf16, head_dim <= 128) matrix-core prefill row tiles;
 // writes partition p of every single-query sequence's query and partition 0
