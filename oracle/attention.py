@@ -62,15 +62,24 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
 
 
 def f64_to_bf16_bits(x) -> np.ndarray:
-    """Round float values to the nearest bfloat16, ties to even (bit patterns)."""
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    rounded = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    out = rounded.astype(np.uint16)
-    nan = np.isnan(f)
-    if nan.any():
-        out[nan] = np.uint16(0x7FC0)
+    """Round values to the nearest bfloat16, ties to even, in one step from
+    float64 (bit patterns).  A bfloat16 has 8 significant bits and the float32
+    exponent range: a value of binary exponent e is a multiple of
+    2^max(e - 7, -133) after rounding (2^-133 is the subnormal step), so it is
+    scaled by that power of two, rounded to an integer half-to-even, and
+    scaled back; magnitudes that round past the largest finite value
+    (3.3895e38) become infinite."""
+    v = np.asarray(x, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.uint16)
+    finite = np.isfinite(v)
+    _, e = np.frexp(np.where(finite, v, 1.0))  # v = m * 2^e, 0.5 <= |m| < 1
+    quantum = np.maximum(e - 8, -133)
+    r = np.ldexp(np.round(np.ldexp(np.where(finite, v, 0.0), -quantum)), quantum)
+    with np.errstate(over="ignore"):
+        f = r.astype(np.float32)  # exact: r is a bfloat16 value (or overflows to inf)
+    f = np.where(finite, f, v.astype(np.float32))
+    out = (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    out[np.isnan(v)] = np.uint16(0x7FC0)
     return out
 
 

@@ -8,8 +8,10 @@ expected value by a route other than the oracle's own:
 * ``widen``: bfloat16 bit patterns -> float64 through ``torch``'s own dtype,
 * ``sdpa``: ``torch.nn.functional.scaled_dot_product_attention`` in float64
   on contiguous (unpaged) keys and values, with an explicit mask,
-* ``online_blocks``: the block-by-block running max / running sum loop of
-  "19.2 KV Cache 系统化管理" §19.2.3, restated in NumPy float64.
+* ``chunked_lse_merge``: softmax attention assembled from key chunks cut at
+  arbitrary positions and combined with the log-sum-exp identity -- the
+  property the running max / running sum of "19.2 KV Cache 系统化管理"
+  §19.2.3 rests on, checked without following that loop.
 """
 
 from __future__ import annotations
@@ -75,25 +77,30 @@ def sdpa(q, k, v, scale, causal_offset=None):
     return out[0].permute(1, 0, 2).numpy()
 
 
-def online_blocks(q, k, v, scale, block_size):
-    """The pages' online-softmax loop over blocks of contiguous K/V (one query).
+def chunked_lse_merge(q, k, v, scale, cuts):
+    """Softmax attention of one query, assembled from key chunks.
 
-    ``q`` [H, D], ``k``/``v`` [n, H, D] with equal head counts (MHA, as on the
-    page).  Returns [H, D].
+    ``q`` [H, D], ``k``/``v`` [n, H, D] (equal head counts).  The keys are cut
+    at the sorted positions ``cuts`` (any positions, not block boundaries);
+    each chunk c is summarised on its own by its log-sum-exp
+    ``L_c = log sum_t exp(s_t)`` and its normalised weighted sum ``o_c``, and
+    the chunks are combined with the identity
+    ``softmax(s) . V = sum_c exp(L_c - L) o_c`` with ``L = log sum_c exp(L_c)``
+    (scipy's logsumexp).  Returns [H, D].
     """
-    h, d = q.shape
-    running_max = np.full(h, -np.inf)
-    running_sum = np.zeros(h)
-    acc = np.zeros((h, d))
+    import scipy.special
+
     n = k.shape[0]
-    for start in range(0, n, block_size):
-        kb = k[start:start + block_size]
-        vb = v[start:start + block_size]
-        s = np.einsum("hd,thd->ht", q, kb) * scale
-        new_max = np.maximum(running_max, s.max(axis=1))
-        rescale = np.exp(running_max - new_max)
-        weights = np.exp(s - new_max[:, None])
-        running_sum = running_sum * rescale + weights.sum(axis=1)
-        acc = acc * rescale[:, None] + np.einsum("ht,thd->hd", weights, vb)
-        running_max = new_max
-    return acc / running_sum[:, None]
+    edges = [0] + sorted(int(c) for c in cuts if 0 < c < n) + [n]
+    lse, outs = [], []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        if lo == hi:
+            continue
+        s = np.einsum("hd,thd->ht", q, k[lo:hi]) * scale
+        lc = scipy.special.logsumexp(s, axis=1)
+        lse.append(lc)
+        outs.append(np.einsum("ht,thd->hd", np.exp(s - lc[:, None]), v[lo:hi]))
+    lse = np.stack(lse)            # [chunks, H]
+    total = scipy.special.logsumexp(lse, axis=0)
+    w = np.exp(lse - total[None])  # [chunks, H]
+    return np.einsum("ch,chd->hd", w, np.stack(outs))
