@@ -157,9 +157,12 @@ __device__ __forceinline__ int seq_of_tile(const int* cum, int B, int64_t t) {
 // slower (batch-256 GQA decode: 0.2935 -> 0.2880 ms).
 constexpr int kStreamWaves = 2;
 static_assert(PA_WAVES_PER_GROUP <= kStreamWaves, "stream workgroups hold at most 2 waves");
+#ifndef PA_FP8_STREAM_TILE
+#define PA_FP8_STREAM_TILE 32
+#endif
 template <typename T>
 constexpr int stream_tile() {
-  return sizeof(T) == 1 ? PA_FP8_TILE_TOKENS : 2 * PA_TILE_TOKENS;
+  return sizeof(T) == 1 ? PA_FP8_STREAM_TILE : 2 * PA_TILE_TOKENS;
 }
 
 // block_tables is a separate __restrict__ argument: nothing the kernel stores

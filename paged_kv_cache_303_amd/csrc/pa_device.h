@@ -183,6 +183,43 @@ __device__ __forceinline__ void fp8x16_to_f32(const uint4& w, float (&f)[16]) {
   }
 }
 
+// The 16 codes of a 16-byte chunk as 8 bfloat16 pairs in memory order (pair
+// e = codes 2e, 2e + 1, the first in the low half).  Every e4m3 value is a
+// bfloat16 value, so the conversion (scale 1) is exact.
+__device__ __forceinline__ void fp8x16_to_bf16x2(const uint4& w, uint32_t (&b)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[2 * i] = __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u[i], 1.0f, false));
+    b[2 * i + 1] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)u[i], 1.0f, true));
+  }
+}
+
+// Two chunks of 16 codes (rows a and b, the same 16 dims) as 16 bfloat16
+// pairs: pair e = (a's code e, b's code e), a in the low half.  Bytes are
+// interleaved with v_perm_b32, then converted two at a time (exactly).
+__device__ __forceinline__ void fp8x16_pairs_to_bf16x2(const uint4& wa, const uint4& wb,
+                                                       uint32_t (&p)[16]) {
+  const uint32_t ua[4] = {wa.x, wa.y, wa.z, wa.w};
+  const uint32_t ub[4] = {wb.x, wb.y, wb.z, wb.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // bytes (a0, b0, a1, b1) and (a2, b2, a3, b3) of dword i of each row
+    const uint32_t lo = __builtin_amdgcn_perm(ub[i], ua[i], 0x05010400u);
+    const uint32_t hi = __builtin_amdgcn_perm(ub[i], ua[i], 0x07030602u);
+    p[4 * i] = __builtin_bit_cast(uint32_t,
+                                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false));
+    p[4 * i + 1] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true));
+    p[4 * i + 2] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false));
+    p[4 * i + 3] = __builtin_bit_cast(uint32_t,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true));
+  }
+}
+
 // Two floats to two e4m3 codes (low byte = a), nearest even.
 __device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;

@@ -138,10 +138,11 @@ struct WaveCtx {
   int nb_max, bs_mask;
   float qk_scale;
   float m_run[G], l_run[G], acc[G][CPL][VEC];
-  // fp8: the current query's 16 dims of this lane's chunk, per head, as floats
-  // (held in registers for the whole sequence: each K chunk is converted once
-  // per tile and dotted with all G heads)
-  float qf[QREG ? G : 1][QREG ? 16 : 1];
+  // fp8: the current query's 16 dims of this lane's chunk, per head, as 8
+  // bfloat16 pairs (held in registers for the whole sequence: each K chunk is
+  // converted once per tile to bfloat16 pairs, exactly -- every e4m3 value is
+  // a bfloat16 value -- and dotted with all G heads by v_dot2_f32_bf16)
+  uint32_t qp[QREG ? G : 1][QREG ? 8 : 1];
 
   __device__ WaveCtx(const DecodeArgs& args, int kv_head, uint4* q_lds)
       : a(args), qs(q_lds), kvh(kv_head) {
@@ -159,19 +160,17 @@ struct WaveCtx {
   // Query token j's chunks of the G heads into LDS; scores stay unscaled and
   // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
   __device__ void load_query(int j) {
-    if constexpr (QREG) {  // bf16 query: every lane widens its chunk's 16 dims per head
+    if constexpr (QREG) {  // bf16 query: every lane keeps its chunk's 16 dims per head
       const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int h = 0; h < QW; ++h) {
           const uint4 v = *(const uint4*)(qrow + (int64_t)g * D + c * VEC + h * 8);
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            qf[g][8 * h + 2 * e] = bf16_lo(w[e]);
-            qf[g][8 * h + 2 * e + 1] = bf16_hi(w[e]);
-          }
+          qp[g][4 * h] = v.x;
+          qp[g][4 * h + 1] = v.y;
+          qp[g][4 * h + 2] = v.z;
+          qp[g][4 * h + 3] = v.w;
         }
       return;
     }
@@ -308,13 +307,13 @@ struct WaveCtx {
     if constexpr (QREG) {  // each chunk of 16 codes converted once, dotted with every head
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        float kf[16];
-        fp8x16_to_f32(tl.k[i][0], kf);
+        uint32_t kb[8];
+        fp8x16_to_bf16x2(tl.k[i][0], kb);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float d = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) d = fmaf(qf[g][e], kf[e], d);
+          for (int e = 0; e < 8; ++e) d = dot2_bf16(qp[g][e], kb[e], d);
           s[i][g] = d;
         }
       }
@@ -419,6 +418,29 @@ struct WaveCtx {
     }
 
     // ---- PV --------------------------------------------------------------------
+    if constexpr (QREG && NI % 2 == 0) {
+      // Two rows at a time, i and i + 1 (same lane, same dims): each dim's two
+      // codes become one bfloat16 pair, and each head's two weights
+      // p * v_scale one pair rounded to bfloat16, so that v_dot2_f32_bf16
+      // adds both rows' terms at once.  Masked rows may hold NaN poison: their
+      // scale and codes are zeroed (code 0 is +0) before any arithmetic.
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const bool va = !(UNIFORM && tail) || (t0 + i * TPI + tg) < end;
+        const bool vb = !(UNIFORM && tail) || (t0 + (i + 1) * TPI + tg) < end;
+        const float sa = select_bits(va, tl.vs[i], 0.f);
+        const float sb = select_bits(vb, tl.vs[i + 1], 0.f);
+        uint32_t vp[16];  // dim e: (row i, row i + 1)
+        fp8x16_pairs_to_bf16x2(mask_words(va, tl.v[i][0]), mask_words(vb, tl.v[i + 1][0]), vp);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const uint32_t wpair = pack_bf16x2(s[i][g] * sa, s[i + 1][g] * sb);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[g][0][e] = dot2_bf16(wpair, vp[e], acc[g][0][e]);
+        }
+      }
+      return;
+    }
     if constexpr (FP8) {  // p * (code * scale): the row's V scale goes into p
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
