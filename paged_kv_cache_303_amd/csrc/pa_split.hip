@@ -48,6 +48,7 @@
 // MFMA operand layout (32x32x16): lane l holds A[l % 32][8 (l / 32) + e] and
 // B[8 (l / 32) + e][l % 32] for e < 8, and D[8 (r / 4) + 4 (l / 32) + r % 4]
 // [l % 32] in accumulator r < 16.
+#include <type_traits>
 #include "pa_wave.h"
 
 namespace pa {
@@ -98,8 +99,8 @@ constexpr size_t split_lds_bytes() {
   constexpr size_t q = (size_t)kSplitWaves * WaveCtx<T, D, G, true>::kQChunks * 16;
   constexpr size_t qn = (size_t)kSplitWaves * WaveCtx<T, D, G, false>::kQChunks * 16;
   size_t m = q > qn ? q : qn;
-  if constexpr (MFMA) {
-    m = m > sizeof(PfTiles<D>) ? m : sizeof(PfTiles<D>);
+  if constexpr (MFMA) {  // two tile buffers (staged and computed alternately), or the merge
+    m = m > 2 * sizeof(PfTiles<D>) ? m : 2 * sizeof(PfTiles<D>);
     m = m > pf_merge_bytes<D>() ? m : pf_merge_bytes<D>();
   }
   return m;
@@ -109,6 +110,16 @@ constexpr size_t split_lds_bytes() {
 // that the 8 keys a lane contributes to one 16-key MFMA step are adjacent.
 __device__ __forceinline__ int vt_quad_slot(int quad) {  // quad = k / 4, 0..7
   return (quad & 4) | ((quad & 1) << 1) | ((quad >> 1) & 1);
+}
+
+// LDS swizzles (XOR of a row's 16-byte chunk index by bits of the row), so
+// that the tile stores, whose lanes write rows 16 (K) or 16 (V^T) apart,
+// fall in different banks; the MFMA operand reads stay 16-byte contiguous.
+__device__ __forceinline__ int k_chunk(int key, int chunk) {  // K row `key`
+  return chunk ^ (((key >> 4) & 1) << 1);
+}
+__device__ __forceinline__ int vt_chunk(int dim, int chunk) {  // V^T row `dim`, 8 keys a chunk
+  return chunk ^ ((dim >> 4) & 3);
 }
 
 // Split point of a prefill chunk's keys: half of its cached context, in
@@ -132,7 +143,7 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
   constexpr int UH = 8 * CPR;  // load units per key half: (key quad, column chunk)
   constexpr int NU = kPfKeySplit * UH;  // units per step, each loaded for K and for V
   static_assert(2 * NU <= kSplitWaves * kWave, "one K or V unit per thread");
-  PfTiles<D>& tl = *reinterpret_cast<PfTiles<D>*>(lds);
+  PfTiles<D>* tiles = reinterpret_cast<PfTiles<D>*>(lds);  // two buffers
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -183,39 +194,74 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
   const bool is_v = (tid / NU) & 1;
   const bool storer = tid < 2 * NU;
   const int u = tid % NU;
-  const int uh = u / UH, uqd = (u % UH) & 7, udc = (u % UH) >> 3;
+  // With 64 or more units per half a wave's units share their half, so its
+  // tiles are wave-uniform and the table entries can be scalar loads (counted
+  // apart from the vector loads in flight); blocks of >= 4 keys put a 32-key
+  // tile in at most 8 consecutive table entries.
+  constexpr bool SCALAR = QUAD && UH % kWave == 0;
+  const int uh = SCALAR ? __builtin_amdgcn_readfirstlane(u / UH) : u / UH;
+  const int uqd = (u % UH) & 7, udc = (u % UH) >> 3;
   const char* pool = (const char*)(is_v ? a.v_pool : a.k_pool) + (int64_t)kvh * D * 2 + udc * 16;
   auto tile_of = [&](int h, int s) { return h_lo(h) + (s + rot) % max(h_cnt(h), 1); };
   auto key_of = [&](int s, int i) {
     return max(min(k_lo + tile_of(uh, s) * kPfTile + 4 * uqd + i, k_hi - 1), 0);
   };
   u32x4_t buf[2][4];
-  int ph[2][4];
-  auto lookup = [&](int s) {
-    // with QUAD a key quad lies in one block, otherwise each key looks its block up
-    ph[s & 1][0] = bt[key_of(s, 0) >> a.log2_bs];
-    if constexpr (!QUAD) {
+  int ph[2][SCALAR ? 8 : 4];
+  const int tile_blocks = max(kPfTile >> a.log2_bs, 1);
+  // table-entry slot of step s: s % 2, a compile-time argument so that the
+  // entries stay in registers
+  auto lookup = [&](int s, auto slot) {
+    constexpr int sl = decltype(slot)::value;
+    if constexpr (SCALAR) {
+      // the entries of the tile's blocks (entries past the table row repeat
+      // the row's last one; their keys are masked)
+      const int b0 = (k_lo + tile_of(uh, s) * kPfTile) >> a.log2_bs;
+      const int last = min(tile_blocks, a.max_blocks - b0) - 1;
 #pragma unroll
-      for (int i = 1; i < 4; ++i) ph[s & 1][i] = bt[key_of(s, i) >> a.log2_bs];
+      for (int j = 0; j < 8; ++j) ph[sl][j] = bt[b0 + min(j, last)];
+    } else {
+      // with QUAD a key quad lies in one block, otherwise each key looks its block up
+      ph[sl][0] = bt[key_of(s, 0) >> a.log2_bs];
+      if constexpr (!QUAD) {
+#pragma unroll
+        for (int i = 1; i < 4; ++i) ph[sl][i] = bt[key_of(s, i) >> a.log2_bs];
+      }
     }
   };
-  auto gather = [&](int s, u32x4_t (&r)[4]) {
+  auto gather = [&](int s, auto slot, u32x4_t (&r)[4]) {
+    constexpr int sl = decltype(slot)::value;
+    int quad_block = 0;
+    if constexpr (SCALAR) {  // this lane's quad: entry j of the tile's blocks
+      const int b0 = (k_lo + tile_of(uh, s) * kPfTile) >> a.log2_bs;
+      const int j = min((key_of(s, 0) >> a.log2_bs) - b0, 7);
+      // a select tree on the bits of j (the entries are wave-uniform)
+      const int* e = ph[sl];
+      const int t0 = j & 1 ? e[1] : e[0], t1 = j & 1 ? e[3] : e[2];
+      const int t2 = j & 1 ? e[5] : e[4], t3 = j & 1 ? e[7] : e[6];
+      const int u0 = j & 2 ? t1 : t0, u1 = j & 2 ? t3 : t2;
+      quad_block = j & 4 ? u1 : u0;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int phys = min(max(ph[s & 1][QUAD ? 0 : i], 0), a.num_blocks - 1);
+      const int entry = SCALAR ? quad_block : ph[sl][QUAD ? 0 : i];
+      const int phys = min(max(entry, 0), a.num_blocks - 1);
       r[i] = *(const u32x4_t*)(pool + (int64_t)phys * block_bytes +
                                (uint32_t)((key_of(s, i) & bs_mask) * (uint32_t)row_bytes));
     }
   };
-  auto stage = [&](int s, const u32x4_t (&r)[4]) {  // registers -> LDS
+  auto stage = [&](int s, const u32x4_t (&r)[4], PfTiles<D>& tl) {  // registers -> LDS
     if (!storer || s >= h_cnt(uh)) return;
     if (!is_v) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(u32x4_t*)&tl.k[uh][4 * uqd + i][udc * 8] = r[i];
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * uqd + i;
+        *(u32x4_t*)&tl.k[uh][key][k_chunk(key, udc) * 8] = r[i];
+      }
       return;
     }
     // V^T: dim 8 dc + 2c + h of the four keys as one 8-byte row segment
-    const int col = 4 * vt_quad_slot(uqd);
+    const int slot = vt_quad_slot(uqd);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -223,29 +269,51 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
         const uint32_t sel = h ? 0x07060302u : 0x05040100u;
         const uint32_t lo = __builtin_amdgcn_perm(r[1][c], r[0][c], sel);
         const uint32_t hi = __builtin_amdgcn_perm(r[3][c], r[2][c], sel);
-        *(uint2*)&tl.vt[uh][udc * 8 + 2 * c + h][col] = make_uint2(lo, hi);
+        const int dim = udc * 8 + 2 * c + h;
+        *(uint2*)&tl.vt[uh][dim][vt_chunk(dim, slot >> 1) * 8 + (slot & 1) * 4] =
+            make_uint2(lo, hi);
       }
     }
   };
 
-  auto step = [&](int s, u32x4_t (&r)[4]) {
-    __syncthreads();  // the previous step's readers are done with the tiles
-    stage(s, r);
-    __syncthreads();
-    // the lookup of step s + 3 before the gather of step s + 2
-    lookup(s + 3);
-    gather(s + 2, r);  // in flight during the next two computes
+  // Step s: compute from tile buffer s % 2 while the rows of step s + 1 are
+  // stored into the other buffer (loaded two steps before), then gather step
+  // s + 3 into the registers just freed and look up step s + 4; one barrier.
+  auto compute = [&](int s, const PfTiles<D>& tl) {
     if (s >= h_cnt(kh)) return;
     const int k0 = k_lo + tile_of(kh, s) * kPfTile;
     if (k0 > wave_last) return;  // no row of this wave sees the tile
     // ---- S^T = K Q^T ------------------------------------------------------
+    // Every fragment read is issued before the first product, so that the
+    // reads overlap one another rather than each waiting alone (where the
+    // registers allow: the per-key table entries of small blocks take some).
     f32x16_t st;
 #pragma unroll
     for (int r2 = 0; r2 < 16; ++r2) st[r2] = 0.f;
+    auto k_frag = [&](int kk) {
+      const int key = lane & 31;
+      return *(const u32x4_t*)&tl.k[kh][key][k_chunk(key, 2 * kk + (lane >> 5)) * 8];
+    };
+    u32x4_t kf[KC];
+    if constexpr (QUAD) {
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      const u32x4_t kf = *(const u32x4_t*)&tl.k[kh][lane & 31][16 * kk + 8 * (lane >> 5)];
-      st = mfma32(kf, qf[kk], st);
+      for (int kk = 0; kk < KC; ++kk) kf[kk] = k_frag(kk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) st = mfma32(QUAD ? kf[kk] : k_frag(kk), qf[kk], st);
+    auto v_frag = [&](int h, int db) {
+      const int dim = 32 * db + (lane & 31);
+      return *(const u32x4_t*)&tl.vt[kh][dim][vt_chunk(dim, 2 * h + (lane >> 5)) * 8];
+    };
+    // the V^T fragments, read while the softmax below runs
+    u32x4_t vf[2][DB];
+    if constexpr (QUAD) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vf[h][db] = v_frag(h, db);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- online softmax of the lane's row (log2 domain) ----------------------
     // Scores stay unscaled until the exponent: scale*log2(e) > 0 keeps the
@@ -294,27 +362,48 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
     for (int h = 0; h < 2; ++h) {
       const u32x4_t pf = {pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4_t vf =
-            *(const u32x4_t*)&tl.vt[kh][32 * db + (lane & 31)][16 * h + 8 * (lane >> 5)];
-        o[db] = mfma32(vf, pf, o[db]);
-      }
+      for (int db = 0; db < DB; ++db) o[db] = mfma32(QUAD ? vf[h][db] : v_frag(h, db), pf, o[db]);
     }
   };
 
-  lookup(0);
-  lookup(1);
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  auto step = [&](int s, auto slot, const PfTiles<D>& cur, PfTiles<D>& next,
+                  u32x4_t (&r)[4]) {  // slot: s % 2
+    using Other = std::integral_constant<int, 1 - decltype(slot)::value>;
+    compute(s, cur);
+    stage(s + 1, r, next);  // r holds the rows of step s + 1
+    if constexpr (SCALAR) {
+      // scalar loads complete out of order: a use waits for all of them, so
+      // the gathers are addressed before the next entries are requested
+      gather(s + 3, Other{}, r);
+      lookup(s + 4, slot);
+    } else {
+      // vector loads complete in order: the entries go first so that the
+      // next step's gathers need not wait for this step's
+      lookup(s + 4, slot);
+      gather(s + 3, Other{}, r);  // in flight during the next two computes
+    }
+    __syncthreads();
+  };
+
+  lookup(0, Slot0{});
+  lookup(1, Slot1{});
   // Wait for the query and the first table entries here: the loop keeps
   // gathers in flight across its compute, and the compiler cannot otherwise
   // prove these loads are done on every path into it (it would wait on the
   // gathers before each MFMA instead).
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  gather(0, buf[0]);
-  lookup(2);
-  gather(1, buf[1]);
+  gather(0, Slot0{}, buf[0]);
+  gather(1, Slot1{}, buf[1]);
+  lookup(2, Slot0{});  // (two entry slots: step s's lookup reuses step s - 2's)
+  stage(0, buf[0], tiles[0]);
+  lookup(3, Slot1{});
+  gather(2, Slot0{}, buf[0]);
+  __syncthreads();
   for (int s = 0; s < nsteps; s += 2) {  // an odd count ends with an idle step
-    step(s, buf[0]);
-    step(s + 1, buf[1]);
+    step(s, Slot0{}, tiles[0], tiles[1], buf[1]);
+    step(s + 1, Slot1{}, tiles[1], tiles[0], buf[0]);
   }
 
   // ---- merge the two key halves of each row block --------------------------------
