@@ -477,7 +477,8 @@ def _calibration_copy(binding, k_pool, v_pool, mib, dev):
 
 
 def _traffic(path):
-    """HBM bytes per launch of the split kernel, from rocprofv3 counters, if current."""
+    """HBM bytes per launch of the measured decode kernels, from rocprofv3 counters, if
+    they were taken on the current version of those kernels' source."""
     if not os.path.exists(path):
         return None
     try:
@@ -485,7 +486,7 @@ def _traffic(path):
     except (OSError, ValueError):
         return None
     from paged_kv_cache_303_amd import build as pa_build
-    if data.get("kernel_source_hash") != pa_build.source_hash():
+    if data.get("kernel_source_hash") != pa_build.source_hash(data.get("kernel_source")):
         return None
     return data.get("bytes_per_launch")
 

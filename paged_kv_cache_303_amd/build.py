@@ -92,11 +92,16 @@ def build(verbose: bool = False, defines=(), out: str | None = None) -> str:
     return out
 
 
-def source_hash() -> str:
-    """SHA-256 over the kernel sources and headers (ties measurements to a version)."""
+def source_hash(source: str | None = None) -> str:
+    """SHA-256 over the kernel sources and headers (ties measurements to a version).
+
+    With ``source`` (a file name under csrc/, e.g. ``"pa_decode.hip"``) only that
+    source and the headers count, so a measurement of its kernels stays current
+    while other sources change."""
     import hashlib
     h = hashlib.sha256()
-    files = sources() + sorted(glob.glob(os.path.join(CSRC, "*.h")))
+    srcs = sources() if source is None else [os.path.join(CSRC, source)]
+    files = srcs + sorted(glob.glob(os.path.join(CSRC, "*.h")))
     files.append(os.path.join(ROOT, "include", "pa.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
