@@ -31,6 +31,11 @@ COMMON = [
     "-mcode-object-version=5",
     "-Wall",
     "-Wno-unused-result",
+    # No NaN semantics for float operations: max reductions and compares need
+    # no quieting or canonicalising.  Nothing that keeps NaN-poisoned rows out
+    # of the sums is a float operation (masks select integer bit patterns, and
+    # gathers past a range's end are clamped to valid rows), so the flag
+    # cannot fold them away.
     "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",
