@@ -131,7 +131,99 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp,
 }
 
 // One wave per (query token, query head); kReduceWaves heads per workgroup.
+// Lane l owns dims [VEC l, VEC l + VEC) of the row (VEC = max(D / 64, 1)) and
+// the weight exp(lse_p - m) of partition p = l (per 64 partitions); the
+// partitions' rows are loaded 8 or 16 at a time, all in flight together
+// (the first batch already while the weights are computed), and summed in
+// partition order with the weights read from their lanes.
 constexpr int kReduceWaves = 4;
+
+template <int VEC>
+__device__ __forceinline__ void reduce_row(const ReduceArgs& a, int64_t row, int nparts,
+                                           int lane) {
+  constexpr int kReduceBatch = VEC >= 4 ? 8 : 16;  // rows in flight per lane
+  const int D = a.head_dim;
+  const float* lse = a.part_lse + row * a.max_partitions;
+  const float* po = a.part_o + row * a.max_partitions * D;
+  const int d0 = lane * VEC;
+  const bool active = d0 < D;  // (head_dim 32: the upper half of the wave idles)
+  auto load = [&](int p, float (&v)[VEC]) {
+    const float* src = po + (int64_t)p * D + d0;
+    if constexpr (VEC == 4) {
+      const float4 x = active ? *(const float4*)src : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else if constexpr (VEC == 2) {
+      const float2 x = active ? *(const float2*)src : make_float2(0.f, 0.f);
+      v[0] = x.x; v[1] = x.y;
+    } else {
+      v[0] = active ? *src : 0.f;
+    }
+  };
+  // rows p0 .. p0 + kReduceBatch - 1 of the n partitions (those past n are not read)
+  auto load_batch = [&](int p0, int n, float (&v)[kReduceBatch][VEC]) {
+#pragma unroll
+    for (int i = 0; i < kReduceBatch; ++i) {
+      if (p0 + i < n) {
+        load(p0 + i, v[i]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[i][e] = 0.f;
+      }
+    }
+  };
+  // the first batch of rows is requested before the weights are known
+  float first[kReduceBatch][VEC];
+  load_batch(0, nparts, first);
+  float m = -INFINITY;
+  for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
+  m = reduce_levels<0, 6>(m, OpMax());
+  float wsum = 0.f;
+  for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
+  wsum = reduce_levels<0, 6>(wsum, OpSum());
+  const float inv = nparts > 0 ? 1.f / wsum : 0.f;
+
+  float o[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) o[e] = 0.f;
+  for (int pc = 0; pc < nparts; pc += kWave) {
+    const int n = min(kWave, nparts - pc);
+    const float wl = lane < n ? __expf(lse[pc + lane] - m) : 0.f;
+    auto weight = [&](int p) {  // p is wave-uniform
+      return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), p));
+    };
+    for (int p = 0; p < n; p += kReduceBatch) {
+      float v[kReduceBatch][VEC];
+      if (pc + p == 0) {
+#pragma unroll
+        for (int i = 0; i < kReduceBatch; ++i)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[i][e] = first[i][e];
+      } else {
+        load_batch(pc + p, pc + n, v);
+      }
+#pragma unroll
+      for (int i = 0; i < kReduceBatch; ++i) {
+        if (p + i < n) {
+          const float w = weight(p + i);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) o[e] = fmaf(w, v[i][e], o[e]);
+        }
+      }
+    }
+  }
+  if (active) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const float x = o[e] * inv;
+      if (a.out_dtype == PA_BF16)
+        ((__bf16*)a.out)[row * D + d0 + e] = (__bf16)x;
+      else
+        ((float*)a.out)[row * D + d0 + e] = x;
+    }
+  }
+  if (a.lse_out != nullptr && lane == 0)
+    a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
+}
 
 __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs a) {
   const int j = blockIdx.x;
@@ -141,10 +233,16 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
 
   int b = j, q_first = j, q_len = 1;
   if (a.cu_q_lens != nullptr) {
-    int lo = 0, hi = a.num_seqs - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (a.cu_q_lens[mid] <= j) lo = mid; else hi = mid - 1;
+    // the last b with cu_q_lens[b] <= j: each round reads 64 entries at once
+    // (one per lane) and keeps the span between the last two that qualify
+    int lo = 0, n = a.num_seqs;  // b in [lo, lo + n)
+    while (n > 1) {
+      const int step = (n + kWave - 1) / kWave;
+      const int i = lo + lane * step;
+      const bool le = lane * step < n && a.cu_q_lens[i] <= j;
+      const int k = 63 - __builtin_clzll(__ballot(le) | 1ull);  // last lane that qualifies
+      lo += k * step;
+      n = min(step, n - k * step);
     }
     b = lo;
     q_first = a.cu_q_lens[b];
@@ -162,40 +260,12 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
   }
   nparts = min(nparts, a.max_partitions);
 
-  const int D = a.head_dim;
   const int64_t row = (int64_t)j * a.num_q_heads + h;
-  const float* lse = a.part_lse + row * a.max_partitions;
-  const float* po = a.part_o + row * a.max_partitions * D;
-  float m = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
-  m = reduce_levels<0, 6>(m, OpMax());
-  float wsum = 0.f;
-  for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
-  wsum = reduce_levels<0, 6>(wsum, OpSum());
-  const float inv = nparts > 0 ? 1.f / wsum : 0.f;
-
-  for (int d = lane; d < D; d += kWave) {
-    float o = 0.f;
-    int p = 0;
-    for (; p + 4 <= nparts; p += 4) {  // four partitions in flight
-      const float v0 = po[(int64_t)(p + 0) * D + d];
-      const float v1 = po[(int64_t)(p + 1) * D + d];
-      const float v2 = po[(int64_t)(p + 2) * D + d];
-      const float v3 = po[(int64_t)(p + 3) * D + d];
-      o = fmaf(__expf(lse[p + 0] - m), v0, o);
-      o = fmaf(__expf(lse[p + 1] - m), v1, o);
-      o = fmaf(__expf(lse[p + 2] - m), v2, o);
-      o = fmaf(__expf(lse[p + 3] - m), v3, o);
-    }
-    for (; p < nparts; ++p) o = fmaf(__expf(lse[p] - m), po[(int64_t)p * D + d], o);
-    o *= inv;
-    if (a.out_dtype == PA_BF16)
-      ((__bf16*)a.out)[row * D + d] = (__bf16)o;
-    else
-      ((float*)a.out)[row * D + d] = o;
+  switch (a.head_dim) {
+    case 256: reduce_row<4>(a, row, nparts, lane); break;
+    case 128: reduce_row<2>(a, row, nparts, lane); break;
+    default: reduce_row<1>(a, row, nparts, lane); break;  // 32, 64
   }
-  if (a.lse_out != nullptr && lane == 0)
-    a.lse_out[row] = nparts > 0 ? m + __logf(wsum) : -INFINITY;
 }
 
 // Block copies between two pools (swap out to / in from pinned host memory,

@@ -222,6 +222,18 @@ def test_split_partials_match_oracle(pa, dtype):
         np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=tol)
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("head_dim", [32, 128, 256])
+def test_reduce_many_partitions(pa, dtype, head_dim):
+    """More partitions than a wave has lanes (the merge takes them 64 at a time),
+    and counts around its batch of rows."""
+    w = wl.custom_decode(21 + head_dim, [1100, 1030, 1024, 257, 255, 64, 1], num_blocks=512,
+                         block_size=16, num_q_heads=8, num_kv_heads=2, head_dim=head_dim,
+                         dtype=dtype, partition_size=16, name=f"many_parts_d{head_dim}")
+    st_p, st_o = _both(pa, w)
+    _check_all_paths(pa, w, st_p, st_o, partitions=(None,))
+
+
 @pytest.mark.parametrize("lens", [
     [3000, 1, 2],                      # one sequence spans many slices
     [1] * 300,                         # fewer tiles than slices
