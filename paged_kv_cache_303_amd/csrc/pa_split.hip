@@ -200,7 +200,12 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
   // tile in at most 8 consecutive table entries.
   constexpr bool SCALAR = QUAD && UH % kWave == 0;
   const int uh = SCALAR ? __builtin_amdgcn_readfirstlane(u / UH) : u / UH;
-  const int uqd = (u % UH) & 7, udc = (u % UH) >> 3;
+  // K units take a row's chunks on neighbouring lanes (each load instruction
+  // reads whole 128-byte lines, which the cache takes in one access per line);
+  // V units take neighbouring quads, so that the transposed stores below fall
+  // in different LDS banks.
+  const int uqd = is_v ? (u % UH) & 7 : (u % UH) / CPR;
+  const int udc = is_v ? (u % UH) >> 3 : (u % UH) % CPR;
   const char* pool = (const char*)(is_v ? a.v_pool : a.k_pool) + (int64_t)kvh * D * 2 + udc * 16;
   auto tile_of = [&](int h, int s) { return h_lo(h) + (s + rot) % max(h_cnt(h), 1); };
   auto key_of = [&](int s, int i) {
