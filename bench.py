@@ -154,6 +154,11 @@ def main():
     per_call = np.array([a.elapsed_time(b) for a, b in events])
     decode_ms = float(per_call.mean())
 
+    # the cache write alone: one new token per sequence through the slot mapping
+    kvw_ms = _timed(lambda: binding.kv_write(k_pool, v_pool, k_tok, v_tok, slot_d),
+                    args.steps, args.warmup)
+    kvw_bytes = len(seq_lens) * (2 * 2 * w.num_kv_heads * w.head_dim * 2 + 4)
+
     # the fixed-partition path (split + reduce), for context
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -216,6 +221,12 @@ def main():
             "kv_GBps": round(kv_bytes / (decode_ms * 1e-3) / 1e9, 1),
             "queries_per_s": round(len(seq_lens) / (decode_ms * 1e-3), 1),
         },
+        "kv_write": {
+            "ms": round(kvw_ms, 4),
+            "bytes": int(kvw_bytes),
+            "GBps": round(kvw_bytes / (kvw_ms * 1e-3) / 1e9, 1),
+        },
+        "gpu": _gpu_info(),
         "split_path": {
             "partition_size": args.partition,
             "ms": round(split_ms, 4),
@@ -489,6 +500,25 @@ def _traffic(path):
     if data.get("kernel_source_hash") != pa_build.source_hash(data.get("kernel_source")):
         return None
     return data.get("bytes_per_launch")
+
+
+def _gpu_info():
+    """Device name and the current and maximum engine clocks rocm-smi reports, if it can."""
+    import subprocess
+    import torch
+    info = {"name": torch.cuda.get_device_name(0), "sclk_mhz": None}
+    try:
+        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        data = json.loads(res.stdout)
+        card = next(iter(data.values()))
+        for k, v in card.items():
+            if "sclk" in k.lower():
+                info["sclk_mhz"] = v
+                break
+    except Exception:  # the clock is context only; its absence changes nothing else
+        pass
+    return info
 
 
 def _cpu_model():

@@ -31,9 +31,11 @@
 //
 // Prefill item (8 waves): wave w takes row block w % 4 (32 rows) and key half
 // w / 4 of the item's key range, in tiles of 32 keys.  Per step the workgroup
-// gathers the two halves' K tiles into LDS as [key][dim] and their V tiles
-// transposed as [dim][key] (each K/V byte gathered once serves 128 rows);
-// each wave then computes
+// brings the two halves' K and V tiles into LDS (each K/V byte loaded once
+// serves 128 rows): with LDS-direct loads as [key][dim] for blocks of at
+// least 4 keys (V^T then read with transposing LDS reads), otherwise through
+// registers, K as [key][dim] and V transposed as [dim][key]; each wave then
+// computes
 //   S^T = K Q^T            v_mfma_f32_32x32x16_bf16, K from LDS, Q in registers
 //   online softmax         per row, in registers, log2 domain, lazy rescale
 //   O^T += V^T P^T         the same MFMA, V^T from LDS, P^T in registers
@@ -67,7 +69,15 @@ constexpr float kLn2Split = 0.69314718055994530942f;
 // s_waitcnt operand: vector-memory count 0, the other counters unconstrained
 // (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm0 = 0x0F70;
+constexpr int kWaitLgkm0 = 0xC07F;  // LDS / scalar-memory count 0, the others unconstrained
+constexpr int kWaitLgkmMask = 0xF0FF;  // AND-ed into a vmcnt wait: lgkmcnt 0 as well
+constexpr int vm_wait(int n) {  // vmcnt n (< 64), the other counters unconstrained
+  return 0x0F70 | (n & 15) | ((n >> 4) << 14);
+}
 
+#ifndef PA_PF_DMA
+#define PA_PF_DMA 1  // prefill tiles through LDS-direct loads (blocks of >= 4 keys)
+#endif
 #ifndef PA_SPLIT_ORDER
 #define PA_SPLIT_ORDER 0  // 0: prefill blocks spread among decode blocks; 1: decode first
 #endif
@@ -88,6 +98,18 @@ struct PfTiles {
   uint16_t k[kPfKeySplit][kPfTile][D + kPfPad];
   uint16_t vt[kPfKeySplit][D][kPfTile + kPfPad];
 };
+// The same with LDS-direct loads: K and V both [key][dim], unpadded rows
+// whose 16-byte chunks are swizzled by key; three of them in flight.
+template <int D>
+struct PfDmaTiles {
+  uint16_t k[kPfKeySplit][kPfTile][D];
+  uint16_t v[kPfKeySplit][kPfTile][D];
+};
+#ifndef PA_PF_STAGES
+#define PA_PF_STAGES 3
+#endif
+constexpr int kPfStages = PA_PF_STAGES;  // 3 or 4
+static_assert(kPfStages == 3 || kPfStages == 4, "three or four tile buffers");
 // The merge of key halves after the loop reuses the same LDS: per row block,
 // m and l of the lane's row and the lane's D/2 accumulators.
 template <int D>
@@ -101,6 +123,9 @@ constexpr size_t split_lds_bytes() {
   size_t m = q > qn ? q : qn;
   if constexpr (MFMA) {  // two tile buffers (staged and computed alternately), or the merge
     m = m > 2 * sizeof(PfTiles<D>) ? m : 2 * sizeof(PfTiles<D>);
+#if PA_PF_DMA
+    m = m > kPfStages * sizeof(PfDmaTiles<D>) ? m : kPfStages * sizeof(PfDmaTiles<D>);
+#endif
     m = m > pf_merge_bytes<D>() ? m : pf_merge_bytes<D>();
   }
   return m;
@@ -453,6 +478,313 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill item with LDS-direct gathers (blocks of at least 4 keys).  Same work
+// and arithmetic as prefill_item; only the way K and V reach LDS differs:
+//   * Every K/V row goes from HBM straight into LDS with a 16-byte
+//     global_load_lds per lane (one instruction fills 1 KiB: 512 / D rows),
+//     so no register staging and no LDS stores.  Rows are unpadded; their
+//     16-byte chunks are XOR-swizzled by key through the choice of source
+//     address (LDS position p of row k holds chunk p ^ f(k)).
+//   * V stays [key][dim]; the V^T operand of O^T += V^T P^T is read with the
+//     transposing ds_read_b64_tr_b16 (within 16 lanes, lane j receives
+//     element j % 4 of the 8-byte reads of lanes j / 4 + 4 e, e < 4), two
+//     reads per 8 keys.
+//   * kPfStages tile buffers: step s is computed from buffer s % S while
+//     the rows of the next S - 1 steps land in the others.
+// Counters on the 512-token chunk: no LDS bank conflicts (the register-staged
+// tile below has them on about half of its LDS cycles) and the same or
+// slightly better time.
+// ---------------------------------------------------------------------------
+// Chunk positions, for an LDS of 64 four-byte banks (16 lanes of a 16-byte
+// read, or 32 lanes of an 8-byte read, are served together): the K reads of
+// 16 consecutive keys and the transposed V reads of 4 consecutive keys x 32
+// bytes (two 16-lane groups at once) each touch every bank once.
+template <int D>
+__device__ __forceinline__ int k_pos(int key, int c) {
+  constexpr int CPR = D / 8;
+  return c ^ ((key * CPR / 16) & (CPR - 1));
+}
+template <int D>
+__device__ __forceinline__ int v_pos(int key, int c) {
+  return c ^ (D == 128 ? 4 * (key & 3) : D == 64 ? 4 * ((key >> 1) & 1) : 0);
+}
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D, int G>
+__device__ void prefill_item_dma(const DecodeArgs& a, const int32_t* __restrict__ bt, char* lds,
+                                 int q_first, int q_len, int len, int r0, int part, int k_lo,
+                                 int k_hi, int kvh) {
+  constexpr int KC = D / 16;           // 16-dim MFMA steps of the QK contraction
+  constexpr int DB = D / 32;           // 32-dim blocks of O^T
+  constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+  constexpr int RPI = 512 / D;         // rows per load instruction (1 KiB)
+  constexpr int NIS = 2 * kPfTile * kPfKeySplit / RPI;  // instructions per step (K and V)
+  constexpr int IPW = NIS / kSplitWaves;                 // per wave
+  static_assert(IPW >= 1 && NIS % kSplitWaves == 0, "whole instructions per wave");
+  PfDmaTiles<D>* tiles = reinterpret_cast<PfDmaTiles<D>*>(lds);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int w = wave_id();
+  const int rb = w % kPfRowBlocks, kh = w / kPfRowBlocks;
+  const int H = a.num_kv_heads;
+  const int rows_total = q_len * G;
+  const int pos_base = len - q_len;
+  const int ntiles = (k_hi - k_lo + kPfTile - 1) / kPfTile;
+  const int bs_mask = (1 << a.log2_bs) - 1;
+  const int64_t row_bytes = (int64_t)H * D * 2;
+  const int64_t block_bytes = row_bytes << a.log2_bs;
+  auto h_lo = [&](int h) { return h * ntiles / kPfKeySplit; };  // first tile of half h
+  auto h_cnt = [&](int h) { return h_lo(h + 1) - h_lo(h); };
+  const int nsteps = h_cnt(kPfKeySplit - 1);  // the last half has the most tiles
+
+  // ---- this wave's rows: Q as the B operand, 8 dims per lane per MFMA -----
+  const int rw0 = r0 + 32 * rb;
+  const int row = min(rw0 + (lane & 31), rows_total - 1);
+  const int lim = pos_base + row / G;  // last key this lane's row sees
+  const int wave_first = pos_base + min(rw0, rows_total - 1) / G;
+  const int wave_last = pos_base + min(rw0 + 31, rows_total - 1) / G;
+  const uint16_t* qrow = (const uint16_t*)a.q +
+                         ((int64_t)(q_first + row / G) * a.num_q_heads + kvh * G + row % G) * D;
+  u32x4_t qf[KC];
+#pragma unroll
+  for (int kk = 0; kk < KC; ++kk) qf[kk] = *(const u32x4_t*)(qrow + 16 * kk + 8 * (lane >> 5));
+
+  float m = -INFINITY, l = 0.f;  // row state (m shared by lanes l, l ^ 32; l partial)
+  f32x16_t o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+
+  // ---- the wave's loads: instructions g = IPW w + j, rows [RPI g', RPI g' + RPI)
+  // of (K or V, half); with these sizes one wave always serves one (K or V, half).
+  const int g0 = IPW * w;
+  const bool is_v = g0 >= NIS / 2;
+  const int lh = (g0 % (NIS / 2)) / (NIS / 4);  // the wave's key half
+  const int key_base = (g0 % (NIS / 4)) * RPI;  // first key of its first instruction
+  const int row_in = lane / CPR, pos = lane % CPR;
+  const char* pool = (const char*)(is_v ? a.v_pool : a.k_pool) + (int64_t)kvh * D * 2;
+  const int rot = blockIdx.x / kQueues;
+  auto tile_of = [&](int h, int s) { return h_lo(h) + (s + rot) % max(h_cnt(h), 1); };
+  const int tile_blocks = max(kPfTile >> a.log2_bs, 1);
+  int ph[2][8];  // table entries of the half's tile, per step parity
+  auto lookup = [&](int s, auto slot) {
+    constexpr int sl = decltype(slot)::value;
+    const int b0 = (k_lo + tile_of(lh, s) * kPfTile) >> a.log2_bs;
+    const int last = min(tile_blocks, a.max_blocks - b0) - 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ph[sl][j] = bt[b0 + min(j, last)];
+  };
+  auto load = [&](int s, auto slot, PfDmaTiles<D>& tl) {
+    constexpr int sl = decltype(slot)::value;
+    const int t0 = k_lo + tile_of(lh, s) * kPfTile;
+    const int b0 = t0 >> a.log2_bs;
+#pragma unroll
+    for (int j = 0; j < IPW; ++j) {
+      const int key = key_base + j * RPI + row_in;  // within the tile
+      const int tk = max(min(t0 + key, k_hi - 1), 0);
+      const int e = min((tk >> a.log2_bs) - b0, 7);
+      const int* ee = ph[sl];
+      const int t_0 = e & 1 ? ee[1] : ee[0], t_1 = e & 1 ? ee[3] : ee[2];
+      const int t_2 = e & 1 ? ee[5] : ee[4], t_3 = e & 1 ? ee[7] : ee[6];
+      const int u_0 = e & 2 ? t_1 : t_0, u_1 = e & 2 ? t_3 : t_2;
+      const int phys = min(max(e & 4 ? u_1 : u_0, 0), a.num_blocks - 1);
+      const int c = is_v ? v_pos<D>(key, pos) : k_pos<D>(key, pos);
+      const char* src = pool + (int64_t)phys * block_bytes +
+                        (uint32_t)((tk & bs_mask) * (uint32_t)row_bytes) + c * 16;
+      uint16_t* dst = is_v ? &tl.v[lh][key_base + j * RPI][0] : &tl.k[lh][key_base + j * RPI][0];
+      const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(
+          (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)dst);
+      // Written out rather than through the builtin: the compiler would treat
+      // the pending LDS writes as aliasing every later LDS read and wait for
+      // all of them (the next steps' rows included) before each compute.  The
+      // waits are explicit instead (barrier_keep_loads, the prologue and the
+      // end of the loop), and no other vector-memory access is issued in the
+      // loop, so the counter holds only these loads.
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src), "s"(lds_addr)
+                   : "memory", "m0");
+    }
+  };
+
+  auto compute = [&](int s, const PfDmaTiles<D>& tl) {
+    if (s >= h_cnt(kh)) return;
+    const int k0 = k_lo + tile_of(kh, s) * kPfTile;
+    if (k0 > wave_last) return;  // no row of this wave sees the tile
+    // ---- S^T = K Q^T ------------------------------------------------------
+    f32x16_t st;
+#pragma unroll
+    for (int r2 = 0; r2 < 16; ++r2) st[r2] = 0.f;
+    u32x4_t kf[KC];
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) {
+      const int key = lane & 31;
+      kf[kk] = *(const u32x4_t*)&tl.k[kh][key][k_pos<D>(key, 2 * kk + (lane >> 5)) * 8];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < KC; ++kk) st = mfma32(kf[kk], qf[kk], st);
+    // the V^T fragments (transposing reads), read while the softmax below runs
+    u32x4_t vf[2][DB];
+    {
+      const int gq = lane >> 4, i = lane & 15;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          uint32_t wv[4];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int key = 16 * h + 8 * r + 4 * (gq >> 1) + (i >> 2);
+            const int dim = 32 * db + 16 * (gq & 1) + 4 * (i & 3);
+            const uint16_t* p = &tl.v[kh][key][v_pos<D>(key, dim >> 3) * 8 + (dim & 4)];
+            const i16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4_t __attribute__((address_space(3)))*)p);
+            wv[2 * r] = (uint32_t)(uint16_t)x[0] | ((uint32_t)(uint16_t)x[1] << 16);
+            wv[2 * r + 1] = (uint32_t)(uint16_t)x[2] | ((uint32_t)(uint16_t)x[3] << 16);
+          }
+          vf[h][db] = u32x4_t{wv[0], wv[1], wv[2], wv[3]};
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- online softmax of the lane's row (log2 domain) ----------------------
+    const float c = a.scale_log2;
+    float x[16];
+#pragma unroll
+    for (int r2 = 0; r2 < 16; ++r2) x[r2] = st[r2];
+    if (__builtin_amdgcn_readfirstlane((int)(k0 + kPfTile - 1 > wave_first))) {
+      const int room = lim - k0 - 4 * (lane >> 5);
+#pragma unroll
+      for (int r2 = 0; r2 < 16; ++r2)
+        x[r2] = 8 * (r2 >> 2) + (r2 & 3) <= room ? x[r2] : -INFINITY;
+    }
+    float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+    for (int r2 = 2; r2 < 16; r2 += 2) mx = fmaxf(mx, fmaxf(x[r2], x[r2 + 1]));
+    mx = level_step<5>(mx, OpMax()) * c;
+    const bool move = mx > m + kPfLazy;
+    if (__builtin_amdgcn_readfirstlane((int)(__ballot(move) != 0))) {
+      const float m_new = move ? mx : m;
+      const float alpha = m_new == m ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2) o[db][r2] *= alpha;
+    }
+    uint32_t pk[8];
+    const float mm = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int r2 = 0; r2 < 16; r2 += 2) {
+      const float p0 = fast_exp2(fmaf(x[r2], c, -mm));
+      const float p1 = fast_exp2(fmaf(x[r2 + 1], c, -mm));
+      const bf16x2_t pb = __builtin_convertvector(f32x2_t{p0, p1}, bf16x2_t);
+      pk[r2 / 2] = __builtin_bit_cast(uint32_t, pb);
+      l = dot2_bf16(pk[r2 / 2], 0x3F803F80u, l);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t pf = {pk[4 * h], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mfma32(vf[h][db], pf, o[db]);
+    }
+  };
+
+  // The workgroup barrier of the loop: this wave's LDS accesses and its rows
+  // of the next step (all but its last kPfStages - 2 steps' loads) are
+  // complete, then every wave meets.  __syncthreads would also wait for the
+  // rows just requested (they are LDS writes), which would leave nothing in
+  // flight.
+  auto barrier_keep_loads = [&]() {
+    __builtin_amdgcn_s_waitcnt(vm_wait((kPfStages - 2) * IPW) & kWaitLgkmMask);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  // Step s: compute tile s from buffer s % S (S = kPfStages); request the
+  // table entries of step s + S and the rows of step s + S - 1 (into buffer
+  // (s - 1) % S, last read in step s - 1); wait for this wave's rows of step
+  // s + 1, then one barrier makes every wave's rows of step s + 1 visible.
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  auto step = [&](int s, auto slot, int bc) {  // slot: s % 2, bc: s % S
+    using Other = std::integral_constant<int, 1 - decltype(slot)::value>;
+    using Ahead = std::conditional_t<(kPfStages - 1) % 2 == 0, decltype(slot), Other>;
+    using Look = std::conditional_t<kPfStages % 2 == 0, decltype(slot), Other>;
+    compute(s, tiles[bc]);
+    lookup(s + kPfStages, Look{});
+    load(s + kPfStages - 1, Ahead{}, tiles[bc == 0 ? kPfStages - 1 : bc - 1]);
+    barrier_keep_loads();
+  };
+
+  lookup(0, Slot0{});
+  lookup(1, Slot1{});
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the query
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  load(0, Slot0{}, tiles[0]);
+  lookup(2, Slot0{});
+  load(1, Slot1{}, tiles[1]);
+  if constexpr (kPfStages == 4) {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    load(2, Slot0{}, tiles[2]);
+    lookup(3, Slot1{});
+  }
+  barrier_keep_loads();
+  int bc = 0;  // s % S
+  for (int s = 0; s < nsteps; s += 2) {  // an odd count ends with an idle step
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    step(s, Slot0{}, bc);
+    bc = bc == kPfStages - 1 ? 0 : bc + 1;
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    step(s + 1, Slot1{}, bc);
+    bc = bc == kPfStages - 1 ? 0 : bc + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the rows requested past the last step
+
+  // ---- merge the two key halves of each row block --------------------------------
+  l = level_step<5>(l, OpSum());
+  float* sp = reinterpret_cast<float*>(lds) + rb * kWave * (D / 2 + 4);
+  __syncthreads();  // every wave is done with the tiles
+  if (kh == 1) {
+    sp[lane] = m;
+    sp[kWave + lane] = l;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *(float4*)&sp[2 * kWave + ((db * 4 + r4) * kWave + lane) * 4] =
+            make_float4(o[db][4 * r4], o[db][4 * r4 + 1], o[db][4 * r4 + 2], o[db][4 * r4 + 3]);
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m2 = sp[lane], l2 = sp[kWave + lane];
+    const float mn = fmaxf(m, m2);
+    const float a1 = m == mn ? 1.f : fast_exp2(m - mn);
+    const float a2 = m2 == mn ? 1.f : fast_exp2(m2 - mn);
+    l = l * a1 + l2 * a2;
+    const int rr = rw0 + (lane & 31);
+    if (rr < rows_total) {
+      const int64_t jh = (int64_t)(q_first + rr / G) * a.num_q_heads + kvh * G + rr % G;
+      const float inv = 1.f / l;
+      float* po = a.part_o + (jh * a.max_partitions + part) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const float4 v = *(const float4*)&sp[2 * kWave + ((db * 4 + r4) * kWave + lane) * 4];
+          *(float4*)&po[32 * db + 8 * r4 + 4 * (lane >> 5)] =
+              make_float4((o[db][4 * r4] * a1 + v.x * a2) * inv,
+                          (o[db][4 * r4 + 1] * a1 + v.y * a2) * inv,
+                          (o[db][4 * r4 + 2] * a1 + v.z * a2) * inv,
+                          (o[db][4 * r4 + 3] * a1 + v.w * a2) * inv);
+        }
+      if (lane < 32) a.part_lse[jh * a.max_partitions + part] = (mn + __log2f(l)) * kLn2Split;
+    }
+  }
+}
+
 // Inclusive-to-exclusive prefix sums of cnt[1..n] in place (cnt[0] = 0), by
 // one wave.
 __device__ void wave_scan(int* cnt, int n, int lane) {
@@ -596,6 +928,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 1) void split_kernel(
           const int k_end = len - q_len + last_row / G + 1;  // keys the tile's rows see
           const int k_lo = part == 1 ? hsplit : 0;
           const int k_hi = nparts == 2 && part == 0 ? hsplit : k_end;
+#if PA_PF_DMA
+          if constexpr (UNIFORM)
+            prefill_item_dma<D, G>(a, block_tables + (int64_t)b * a.max_blocks, lds, q_first,
+                                   q_len, len, r0, part, k_lo, k_hi, kvh);
+          else
+#endif
           prefill_item<D, G, UNIFORM>(a, block_tables + (int64_t)b * a.max_blocks, lds, q_first,
                                       q_len, len, r0, part, k_lo, k_hi, kvh);
         }
