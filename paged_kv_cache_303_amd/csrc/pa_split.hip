@@ -105,11 +105,7 @@ struct PfDmaTiles {
   uint16_t k[kPfKeySplit][kPfTile][D];
   uint16_t v[kPfKeySplit][kPfTile][D];
 };
-#ifndef PA_PF_STAGES
-#define PA_PF_STAGES 3
-#endif
-constexpr int kPfStages = PA_PF_STAGES;  // 3 or 4
-static_assert(kPfStages == 3 || kPfStages == 4, "three or four tile buffers");
+constexpr int kPfStages = 3;  // tile buffers (rows loaded two steps ahead)
 // The merge of key halves after the loop reuses the same LDS: per row block,
 // m and l of the lane's row and the lane's D/2 accumulators.
 template <int D>
@@ -490,8 +486,8 @@ __device__ void prefill_item(const DecodeArgs& a, const int32_t* __restrict__ bt
 //     transposing ds_read_b64_tr_b16 (within 16 lanes, lane j receives
 //     element j % 4 of the 8-byte reads of lanes j / 4 + 4 e, e < 4), two
 //     reads per 8 keys.
-//   * kPfStages tile buffers: step s is computed from buffer s % S while
-//     the rows of the next S - 1 steps land in the others.
+//   * Three tile buffers: step s is computed from buffer s % 3 while the
+//     rows of steps s + 1 and s + 2 land in the other two.
 // Counters on the 512-token chunk: no LDS bank conflicts (the register-staged
 // tile below has them on about half of its LDS cycles) and the same or
 // slightly better time.
@@ -610,12 +606,12 @@ __device__ void prefill_item_dma(const DecodeArgs& a, const int32_t* __restrict_
     }
   };
 
-  auto compute = [&](int s, const PfDmaTiles<D>& tl) {
-    if (s >= h_cnt(kh)) return;
+  // QK of tile s into st (false: the wave has nothing to do for tile s)
+  auto qk = [&](int s, const PfDmaTiles<D>& tl, f32x16_t& st) -> bool {
+    if (s >= h_cnt(kh)) return false;
     const int k0 = k_lo + tile_of(kh, s) * kPfTile;
-    if (k0 > wave_last) return;  // no row of this wave sees the tile
+    if (k0 > wave_last) return false;  // no row of this wave sees the tile
     // ---- S^T = K Q^T ------------------------------------------------------
-    f32x16_t st;
 #pragma unroll
     for (int r2 = 0; r2 < 16; ++r2) st[r2] = 0.f;
     u32x4_t kf[KC];
@@ -627,6 +623,11 @@ __device__ void prefill_item_dma(const DecodeArgs& a, const int32_t* __restrict_
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < KC; ++kk) st = mfma32(kf[kk], qf[kk], st);
+    return true;
+  };
+  // softmax and PV of tile s, from its scores st
+  auto softmax_pv = [&](int s, const f32x16_t& st, const PfDmaTiles<D>& tl) {
+    const int k0 = k_lo + tile_of(kh, s) * kPfTile;
     // the V^T fragments (transposing reads), read while the softmax below runs
     u32x4_t vf[2][DB];
     {
@@ -695,27 +696,29 @@ __device__ void prefill_item_dma(const DecodeArgs& a, const int32_t* __restrict_
   };
 
   // The workgroup barrier of the loop: this wave's LDS accesses and its rows
-  // of the next step (all but its last kPfStages - 2 steps' loads) are
-  // complete, then every wave meets.  __syncthreads would also wait for the
-  // rows just requested (they are LDS writes), which would leave nothing in
-  // flight.
+  // of the next step (all but its last IPW loads) are complete, then every
+  // wave meets.  __syncthreads would also wait for the rows just requested
+  // (they are LDS writes), which would leave nothing in flight.
   auto barrier_keep_loads = [&]() {
-    __builtin_amdgcn_s_waitcnt(vm_wait((kPfStages - 2) * IPW) & kWaitLgkmMask);
+    __builtin_amdgcn_s_waitcnt(vm_wait(IPW) & kWaitLgkmMask);
     asm volatile("s_barrier" ::: "memory");
   };
-  // Step s: compute tile s from buffer s % S (S = kPfStages); request the
-  // table entries of step s + S and the rows of step s + S - 1 (into buffer
-  // (s - 1) % S, last read in step s - 1); wait for this wave's rows of step
-  // s + 1, then one barrier makes every wave's rows of step s + 1 visible.
+  // Step s: compute tile s from buffer s % 3; request the table entries of
+  // step s + 3 and the rows of step s + 2 (into buffer (s + 2) % 3, last read
+  // in step s - 1); wait for this wave's rows of step s + 1, then one barrier
+  // makes every wave's rows of step s + 1 visible.  (Running the vector work
+  // of key half 1 one tile behind, so that the two waves of a SIMD alternate
+  // between matrix and vector work, was measured slower: 94 against 83 us
+  // for the 512-token chunk.)
   using Slot0 = std::integral_constant<int, 0>;
   using Slot1 = std::integral_constant<int, 1>;
-  auto step = [&](int s, auto slot, int bc) {  // slot: s % 2, bc: s % S
+  auto step = [&](int s, auto slot, int bc) {  // slot: s % 2, bc: s % 3
     using Other = std::integral_constant<int, 1 - decltype(slot)::value>;
-    using Ahead = std::conditional_t<(kPfStages - 1) % 2 == 0, decltype(slot), Other>;
-    using Look = std::conditional_t<kPfStages % 2 == 0, decltype(slot), Other>;
-    compute(s, tiles[bc]);
-    lookup(s + kPfStages, Look{});
-    load(s + kPfStages - 1, Ahead{}, tiles[bc == 0 ? kPfStages - 1 : bc - 1]);
+    const PfDmaTiles<D>& cur = tiles[bc];
+    f32x16_t st;
+    if (qk(s, cur, st)) softmax_pv(s, st, cur);
+    lookup(s + 3, Other{});
+    load(s + 2, slot, tiles[(bc + 2) % kPfStages]);
     barrier_keep_loads();
   };
 
@@ -726,13 +729,8 @@ __device__ void prefill_item_dma(const DecodeArgs& a, const int32_t* __restrict_
   load(0, Slot0{}, tiles[0]);
   lookup(2, Slot0{});
   load(1, Slot1{}, tiles[1]);
-  if constexpr (kPfStages == 4) {
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    load(2, Slot0{}, tiles[2]);
-    lookup(3, Slot1{});
-  }
   barrier_keep_loads();
-  int bc = 0;  // s % S
+  int bc = 0;  // s % 3
   for (int s = 0; s < nsteps; s += 2) {  // an odd count ends with an idle step
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     step(s, Slot0{}, bc);
