@@ -120,15 +120,20 @@ def test_chunked_prefill_small(pa, dtype):
 
 @pytest.mark.parametrize("head_dim", [32, 64, 128, 256])
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
-def test_prefill_shape_grid(pa, head_dim, group):
+@pytest.mark.parametrize("block_size", [8, 32])
+def test_prefill_shape_grid(pa, head_dim, group, block_size):
     """Prefill chunks (the matrix-core tile for bf16): row tiles cut mid-token,
-    several chunks and decode tokens in one launch, partitions of 48 keys
-    (not a multiple of the 32-key tile), block size 8."""
+    several chunks and decode tokens in one launch, partitions of 48 or 64
+    keys (48: not a multiple of the 32-key tile).  Blocks of 32 keys take the
+    LDS-direct tile at every head size; blocks of 8 keys take it only where a
+    decode load instruction spans at most 8 rows, the register-staged tile
+    elsewhere."""
     hkv = 2
     w = wl.custom_decode(60 + head_dim + group, [70, 1, 130, 33, 200], num_blocks=256,
-                         block_size=8, num_q_heads=hkv * group, num_kv_heads=hkv,
+                         block_size=block_size, num_q_heads=hkv * group, num_kv_heads=hkv,
                          head_dim=head_dim, dtype=wl.BF16, q_lens=[70, 1, 37, 1, 65],
-                         partition_size=48, name=f"prefill_d{head_dim}_g{group}")
+                         partition_size=48 if block_size <= 16 else 64,
+                         name=f"prefill_d{head_dim}_g{group}_bs{block_size}")
     st_p, st_o = _both(pa, w)
     _check_all_paths(pa, w, st_p, st_o, partitions=(None, 256))
 
