@@ -52,6 +52,9 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 #ifndef PA_FP8_TILE_TOKENS
 #define PA_FP8_TILE_TOKENS 32  // the same for e4m3 pools (half the bytes per row)
 #endif
+#ifndef PA_FP8_QREG_MAX_G
+#define PA_FP8_QREG_MAX_G 8
+#endif
 #ifndef PA_FP8_QREG_MAX_D
 #define PA_FP8_QREG_MAX_D 256  // fp8 with G <= 4: the query as bfloat16 pairs in registers up to this head size
 #endif
@@ -119,7 +122,7 @@ struct WaveCtx {
   // fp8 with up to 4 heads per KV head and head_dim <= 128: the query in
   // registers (see qf); otherwise in LDS like the other types (registers
   // would not hold it)
-  static constexpr bool QREG = FP8 && G <= 4 && D <= PA_FP8_QREG_MAX_D;
+  static constexpr bool QREG = FP8 && G <= PA_FP8_QREG_MAX_G && D <= PA_FP8_QREG_MAX_D;
 
   struct Tile {
     uint4 k[NI][CPL];
