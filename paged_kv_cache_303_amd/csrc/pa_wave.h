@@ -52,6 +52,9 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 #ifndef PA_FP8_TILE_TOKENS
 #define PA_FP8_TILE_TOKENS 32  // the same for e4m3 pools (half the bytes per row)
 #endif
+#ifndef PA_BF16_PAIR_PV
+#define PA_BF16_PAIR_PV 1  // bf16 PV two rows at a time with v_dot2_f32_bf16
+#endif
 #ifndef PA_FP8_QREG_MAX_G
 #define PA_FP8_QREG_MAX_G 8
 #endif
@@ -443,6 +446,39 @@ struct WaveCtx {
           const uint32_t wpair = pack_bf16x2(s[i][g] * sa, s[i + 1][g] * sb);
 #pragma unroll
           for (int e = 0; e < 16; ++e) acc[g][0][e] = dot2_bf16(wpair, vp[e], acc[g][0][e]);
+        }
+      }
+      return;
+    }
+    if constexpr (BF16 && NI % 2 == 0 && PA_BF16_PAIR_PV) {
+      // Two rows at a time, i and i + 1 (same lane, same dims): each dim's two
+      // values form one bfloat16 pair and each head's two weights one pair
+      // rounded to bfloat16, so that v_dot2_f32_bf16 adds both rows' terms
+      // at once (half the multiply-adds of the fp32 form, and no unpacking).
+      // Masked rows may hold NaN poison: their bits are zeroed first.
+#pragma unroll
+      for (int i = 0; i < NI; i += 2) {
+        const bool va = !(UNIFORM && tail) || (t0 + i * TPI + tg) < end;
+        const bool vb = !(UNIFORM && tail) || (t0 + (i + 1) * TPI + tg) < end;
+        uint32_t wp[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) wp[g] = pack_bf16x2(s[i][g], s[i + 1][g]);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const uint4 a4 = mask_words(va, tl.v[i][k]);
+          const uint4 b4 = mask_words(vb, tl.v[i + 1][k]);
+          const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w};
+          const uint32_t bw[4] = {b4.x, b4.y, b4.z, b4.w};
+          uint32_t vp[8];  // dim 2m + h: (row i, row i + 1)
+#pragma unroll
+          for (int m2 = 0; m2 < 4; ++m2) {
+            vp[2 * m2] = __builtin_amdgcn_perm(bw[m2], aw[m2], 0x05040100u);
+            vp[2 * m2 + 1] = __builtin_amdgcn_perm(bw[m2], aw[m2], 0x07060302u);
+          }
+#pragma unroll
+          for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[g][k][e] = dot2_bf16(wp[g], vp[e], acc[g][k][e]);
         }
       }
       return;

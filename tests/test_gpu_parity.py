@@ -224,7 +224,11 @@ def test_split_partials_match_oracle(pa, dtype):
     tol = 1e-5 if dtype == wl.F32 else 1e-4
     for j, n in enumerate(nparts):
         np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=tol)
-        np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=tol)
+        if dtype == wl.F32:
+            np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=tol)
+        else:  # bf16 probabilities in the P V products (fp32 accumulation)
+            d = np.abs(po[j, :, :n] - o_ref[j, :, :n])
+            assert (d <= 1e-2 + 2e-2 * np.abs(o_ref[j, :, :n])).all(), (j, d.max())
 
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
