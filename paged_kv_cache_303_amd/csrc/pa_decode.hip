@@ -337,9 +337,10 @@ __global__ __launch_bounds__(kFixupWaves * kWave) void stream_fixup_kernel(Decod
   }
 }
 
+// Keys a block must hold for the UNIFORM kernels.
 template <typename T, int D, int G>
 constexpr int tpi() {
-  return Shape<T, D, G>::TPI;
+  return Shape<T, D, G>::UKEYS;
 }
 
 template <typename T, int D, int G>

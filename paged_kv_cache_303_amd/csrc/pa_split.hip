@@ -992,7 +992,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 1) void split_kernel(
 
 template <typename T, int D, int G>
 pa_status launch_split_t(const DecodeArgs& a, hipStream_t stream) {
-  const bool uniform = (1 << a.log2_bs) >= Shape<T, D, G>::TPI;
+  const bool uniform = (1 << a.log2_bs) >= Shape<T, D, G>::UKEYS;
   const void* k = uniform ? (const void*)split_kernel<T, D, G, true>
                           : (const void*)split_kernel<T, D, G, false>;
   const size_t lds = (size_t)2 * (a.num_seqs + 1) * sizeof(int);

@@ -61,6 +61,9 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 #ifndef PA_FP8_QREG_MAX_D
 #define PA_FP8_QREG_MAX_D 256  // fp8 with G <= 4: the query as bfloat16 pairs in registers up to this head size
 #endif
+#ifndef PA_FP8_MFMA_QK
+#define PA_FP8_MFMA_QK 1  // fp8 scores on the matrix cores (see Shape::MQK_OK)
+#endif
 #ifndef PA_MAX_CPL
 #define PA_MAX_CPL 2  // 16-byte chunks of a row per lane, at most
 #endif
@@ -93,6 +96,17 @@ struct Shape {
   static constexpr int NI0 = (TILE_TOKENS / TPI) < 1 ? 1 : (TILE_TOKENS / TPI);
   static constexpr int NI = (NI0 * CPL > MAX_LOADS) ? (MAX_LOADS / CPL < 1 ? 1 : MAX_LOADS / CPL) : NI0;
   static constexpr int TT = NI * TPI;
+  // fp8 scores on the matrix cores (WaveCtx::MQK) where they pay: with 8
+  // heads a KV head or head_dim 256 (MI355X, balanced decode at batch 128:
+  // G = 8, D = 128 3.5 against 2.2 TB/s; G = 4, D = 256 4.7 against 4.4);
+  // at G <= 4, D <= 128 the vector-unit scores are faster (4.4 against 4.0).
+  // Its K loads cover 16 keys an instruction, so it needs blocks of at least
+  // 16 keys for the uniform (one block per instruction) lookup.
+  static constexpr bool MQK_OK = PA_FP8_MFMA_QK && sizeof(T) == 1 && G <= 8 &&
+                                 (D == 64 || D == 128 || D == 256) && TT % 16 == 0 &&
+                                 (G >= 8 || D >= 256);
+  // keys a block must hold for the UNIFORM kernels
+  static constexpr int UKEYS = MQK_OK && TPI < 16 ? 16 : TPI;
   // Ranges start at multiples of 16 (partitions) or of TT (slices), plus
   // multiples of TT, so every load instruction starts on a multiple of TPI
   // (needed by the UNIFORM lookup).
@@ -125,7 +139,20 @@ struct WaveCtx {
   // fp8 with up to 4 heads per KV head and head_dim <= 128: the query in
   // registers (see qf); otherwise in LDS like the other types (registers
   // would not hold it)
-  static constexpr bool QREG = FP8 && G <= PA_FP8_QREG_MAX_G && D <= PA_FP8_QREG_MAX_D;
+  // fp8 scores on the matrix cores: S = Q K^T with v_mfma_f32_16x16x32_bf16
+  // per group of 16 keys (query heads as the 16 rows, G of them real; keys
+  // as the columns; 32 dims a step).  Lane l loads 16 codes of key l % 16 --
+  // bytes 64 ii + 16 (l / 16) of the row for K load ii of the group -- and
+  // feeds codes 8h .. 8h+7 of that load, converted exactly to bfloat16, to
+  // step 2 ii + h; the query's rows are laid out the same way, once per
+  // sequence.  Scores come back with key l % 16 in lane l and heads
+  // 4 (l / 16) + r in its four registers; the softmax runs there, and each
+  // lane then fetches the weights of its V rows for the vector-unit PV.
+  static constexpr bool MQK = S::MQK_OK && UNIFORM;
+  static constexpr int KG = TT / 16;  // 16-key groups per tile
+  static constexpr int LPK = D / 64;  // K loads per group (64 codes per 16 lanes)
+  static constexpr int NU = D / 32;   // matrix steps per group
+  static constexpr bool QREG = FP8 && !MQK && G <= PA_FP8_QREG_MAX_G && D <= PA_FP8_QREG_MAX_D;
 
   struct Tile {
     uint4 k[NI][CPL];
@@ -152,6 +179,10 @@ struct WaveCtx {
   // converted once per tile to bfloat16 pairs, exactly -- every e4m3 value is
   // a bfloat16 value -- and dotted with all G heads by v_dot2_f32_bf16)
   uint32_t qp[QREG ? G : 1][QREG ? 8 : 1];
+  // MQK: the query as the matrix operand (row lane % 16 < G, else zero), per
+  // step, and the lane's partial softmax sums of heads 4 (lane / 16) + r
+  u32x4_t qa[MQK ? NU : 1];
+  float lq[4];
 
   __device__ WaveCtx(const DecodeArgs& args, int kv_head, uint4* q_lds)
       : a(args), qs(q_lds), kvh(kv_head) {
@@ -169,6 +200,18 @@ struct WaveCtx {
   // Query token j's chunks of the G heads into LDS; scores stay unscaled and
   // scale*log2(e) goes into the exponent's fma (bf16) or into the fp32 query.
   __device__ void load_query(int j) {
+    if constexpr (MQK) {
+      const int row = lane & 15;
+      const uint16_t* qrow =
+          (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G + min(row, G - 1)) * D;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int dim = 64 * (u >> 1) + 16 * (lane >> 4) + 8 * (u & 1);
+        const uint4 v = *(const uint4*)(qrow + dim);
+        qa[u] = row < G ? u32x4_t{v.x, v.y, v.z, v.w} : u32x4_t{0u, 0u, 0u, 0u};
+      }
+      return;
+    }
     if constexpr (QREG) {  // bf16 query: every lane keeps its chunk's 16 dims per head
       const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)j * a.num_q_heads + kvh * G) * D;
 #pragma unroll
@@ -223,6 +266,8 @@ struct WaveCtx {
 
   __device__ void reset() {
 #pragma unroll
+    for (int r = 0; r < 4; ++r) lq[r] = 0.f;
+#pragma unroll
     for (int g = 0; g < G; ++g) {
       m_run[g] = -INFINITY;
       l_run[g] = 0.f;
@@ -266,6 +311,35 @@ struct WaveCtx {
       // buffer loads: descriptor of the block (scalar), row offset (scalar),
       // lane offset (one loop-invariant vector register)
       const uint32_t lane_off = (uint32_t)tg * row_bytes + lane_col;
+      if constexpr (MQK) {
+        // K: group kg = keys t0 + 16 kg + (lane & 15), in the block of V
+        // instruction 16 kg / TPI (blocks hold >= 16 keys, groups are aligned)
+        const uint32_t k_off =
+            (uint32_t)(lane & 15) * row_bytes + (uint32_t)(kvh * D + 16 * (lane >> 4));
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg) {
+          const int phys = min(max(ph[16 * kg / TPI], 0), nb_max);
+          const int r0 = (t0 + 16 * kg) & bs_mask;
+          const __amdgpu_buffer_rsrc_t kr =
+              buffer_rsrc(kp + phys * block_bytes, (uint32_t)block_bytes);
+#pragma unroll
+          for (int ii = 0; ii < LPK; ++ii)
+            tl.k[kg * LPK + ii][0] = buffer_load16_nt(kr, k_off + 64 * ii, (uint32_t)r0 * row_bytes);
+          tl.ks[kg] = a.k_scale[(((int64_t)phys << a.log2_bs) + r0 + (lane & 15)) *
+                                    a.num_kv_heads + kvh];
+        }
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int phys = min(max(ph[i], 0), nb_max);
+          const uint32_t row = (uint32_t)((t0 + i * TPI) & bs_mask) * row_bytes;
+          const __amdgpu_buffer_rsrc_t vr =
+              buffer_rsrc(vp + phys * block_bytes, (uint32_t)block_bytes);
+          tl.v[i][0] = buffer_load16_nt(vr, lane_off, row);
+          tl.vs[i] = a.v_scale[(((int64_t)phys << a.log2_bs) + ((t0 + i * TPI) & bs_mask) + tg) *
+                                   a.num_kv_heads + kvh];
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int phys = min(max(ph[i], 0), nb_max);
@@ -305,10 +379,115 @@ struct WaveCtx {
     }
   }
 
+  // MQK scores and softmax of the tile at t0 (keys < end): afterwards s[i][g]
+  // holds the weight of this lane's V row i for head g, as in dot_softmax.
+  __device__ void mqk_softmax(const Tile& tl, int t0, int end, bool tail, float (&s)[NI][G]) {
+    typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const int hsel = lane >> 4;  // heads 4 hsel + r of this lane's scores
+    f32x4_t sc[KG];
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      sc[kg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const uint4 w = tl.k[kg * LPK + (u >> 1)][0];
+        const uint32_t lo = (u & 1) ? w.z : w.x, hi = (u & 1) ? w.w : w.y;
+        const u32x4_t kb = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)lo, 1.0f, true)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, false)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)hi, 1.0f, true))};
+        sc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[u]),
+                                                        __builtin_bit_cast(bf16x8_t, kb), sc[kg],
+                                                        0, 0, 0);
+      }
+    }
+    // the key's K scale; keys past the end (NaN-poisoned codes or scales
+    // possible) get -inf by a bit select
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const bool valid = !tail || (t0 + 16 * kg + (lane & 15)) < end;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[kg][r] = select_bits(valid, sc[kg][r] * tl.ks[kg], -INFINITY);
+    }
+    // ---- online softmax (log2 domain), lazily rescaled ------------------------
+    constexpr int R = G < 4 ? G : 4;  // score registers that hold real heads
+    float mt[G];
+    bool move = false;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float mx = sc[0][r];
+#pragma unroll
+      for (int kg = 1; kg < KG; ++kg) mx = fmaxf(mx, sc[kg][r]);
+      mx = reduce_levels<0, 4>(mx, OpMax());
+#pragma unroll
+      for (int hb = 0; 4 * hb + r < G; ++hb) {
+        const int g = 4 * hb + r;
+        mt[g] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mx), 16 * hb)) *
+                qk_scale;
+        move |= mt[g] > m_run[g] + kLazy;
+      }
+    }
+    if (__builtin_amdgcn_readfirstlane((int)move)) {  // mt and m_run are uniform
+      float alpha[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float m_new = fmaxf(m_run[g], mt[g]);
+        alpha[g] = fast_exp2(m_run[g] - m_new);
+        m_run[g] = m_new;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[g][0][e] *= alpha[g];
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) lq[r] *= (G > 4 && hsel == 1) ? alpha[(4 + r) % G] : alpha[r];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float m = (G > 4 && hsel == 1) ? m_run[(4 + r) % G] : m_run[r];
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {
+        const float p = fast_exp2(fmaf(sc[kg][r], qk_scale, -m));
+        lq[r] += p;
+        sc[kg][r] = p;
+      }
+    }
+    // ---- each lane's V rows: key i TPI + tg of the tile, from lane key % 16
+    // (+ 16 per four heads) of its group's scores
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int key = i * TPI + tg;
+      constexpr int kTPI = TPI;
+      const int kg = (i * kTPI) / 16;  // the same for every lane (TPI divides 16)
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int src = (key & 15) + 16 * (g >> 2);
+        // (the element is copied out first: this compiler's __builtin_bit_cast
+        // of a vector element reads element 0)
+        const float x = sc[kg][g & 3];
+        s[i][g] = __builtin_bit_cast(
+            float, __builtin_amdgcn_ds_bpermute(4 * src, __builtin_bit_cast(int, x)));
+      }
+    }
+  }
+
   // Fold the tile at t0 (keys < end) into the running softmax state.
   __device__ void compute(const Tile& tl, int t0, int end) {
-    // ---- scores: partial dots over the lane's chunks, then sum the row -----
     float s[NI][G];
+    const bool tail = t0 + TT > end;
+    if constexpr (MQK) {
+      mqk_softmax(tl, t0, end, tail, s);
+    } else {
+      dot_softmax(tl, t0, end, tail, s);
+    }
+    pv(tl, t0, end, tail, s);
+  }
+
+  // Scores on the vector units (partial dots over the lane's chunks, summed
+  // over the row's lanes) and the online softmax: afterwards s[i][g] holds the
+  // weight of this lane's row i for head g.
+  __device__ void dot_softmax(const Tile& tl, int t0, int end, bool tail, float (&s)[NI][G]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -382,7 +561,6 @@ struct WaveCtx {
 #pragma unroll
         for (int g = 0; g < G; ++g) s[i][g] *= tl.ks[i];
     }
-    const bool tail = t0 + TT > end;
     if (tail) {  // rows past the end get probability 0
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
@@ -426,8 +604,11 @@ struct WaveCtx {
       }
     }
 
-    // ---- PV --------------------------------------------------------------------
-    if constexpr (QREG && NI % 2 == 0) {
+  }
+
+  // PV of the tile at t0 with the weights s of this lane's rows.
+  __device__ void pv(const Tile& tl, int t0, int end, bool tail, const float (&s)[NI][G]) {
+    if constexpr ((QREG || MQK) && NI % 2 == 0) {
       // Two rows at a time, i and i + 1 (same lane, same dims): each dim's two
       // codes become one bfloat16 pair, and each head's two weights
       // p * v_scale one pair rounded to bfloat16, so that v_dot2_f32_bf16
@@ -557,9 +738,19 @@ struct WaveCtx {
   // Sum the token groups: afterwards lanes with tg == 0 hold the full acc of
   // their chunks and every lane the full l.
   __device__ void combine(float (&l)[G]) {
+    if constexpr (MQK) {  // sums of the 16 key lanes of each head's registers
+#pragma unroll
+      for (int r = 0; r < (G < 4 ? G : 4); ++r) {
+        const float t = reduce_levels<0, 4>(lq[r], OpSum());
+#pragma unroll
+        for (int hb = 0; 4 * hb + r < G; ++hb)
+          l_run[4 * hb + r] =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, t), 16 * hb));
+      }
+    }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      l[g] = reduce_groups<LOG_LPR>(l_run[g], OpSum());
+      l[g] = MQK ? l_run[g] : reduce_groups<LOG_LPR>(l_run[g], OpSum());
 #pragma unroll
       for (int k = 0; k < CPL; ++k)
 #pragma unroll
