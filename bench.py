@@ -503,18 +503,19 @@ def _traffic(path):
 
 
 def _gpu_info():
-    """Device name and the current and maximum engine clocks rocm-smi reports, if it can."""
-    import subprocess
+    """Device name and the engine clock the driver reports as current, read from
+    sysfs (no child process: a program started after the GPU is initialised
+    would be refused on some hosts)."""
+    import glob
     import torch
     info = {"name": torch.cuda.get_device_name(0), "sclk_mhz": None}
     try:
-        res = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                             text=True, timeout=20)
-        data = json.loads(res.stdout)
-        card = next(iter(data.values()))
-        for k, v in card.items():
-            if "sclk" in k.lower():
-                info["sclk_mhz"] = v
+        for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            with open(path) as fh:
+                cur = [l.split(":", 1)[1].strip().rstrip("*").strip()
+                       for l in fh if l.rstrip().endswith("*")]
+            if cur:
+                info["sclk_mhz"] = cur[0]
                 break
     except Exception:  # the clock is context only; its absence changes nothing else
         pass

@@ -62,7 +62,7 @@ struct Elt<uint8_t> {  // e4m3 codes, one fp32 scale per (token, KV head)
 #define PA_FP8_QREG_MAX_D 256  // fp8 with G <= 4: the query as bfloat16 pairs in registers up to this head size
 #endif
 #ifndef PA_FP8_MFMA_QK
-#define PA_FP8_MFMA_QK 1  // fp8 scores on the matrix cores (see Shape::MQK_OK)
+#define PA_FP8_MFMA_QK 1  // fp8 scores on the matrix cores (see Shape::MQK_OK; 2: every shape)
 #endif
 #ifndef PA_MAX_CPL
 #define PA_MAX_CPL 2  // 16-byte chunks of a row per lane, at most
@@ -104,7 +104,7 @@ struct Shape {
   // 16 keys for the uniform (one block per instruction) lookup.
   static constexpr bool MQK_OK = PA_FP8_MFMA_QK && sizeof(T) == 1 && G <= 8 &&
                                  (D == 64 || D == 128 || D == 256) && TT % 16 == 0 &&
-                                 (G >= 8 || D >= 256);
+                                 (G >= 8 || D >= 256 || PA_FP8_MFMA_QK >= 2);
   // keys a block must hold for the UNIFORM kernels
   static constexpr int UKEYS = MQK_OK && TPI < 16 ? 16 : TPI;
   // Ranges start at multiples of 16 (partitions) or of TT (slices), plus
