@@ -116,6 +116,18 @@ def test_fp8_shape_grid(pa, head_dim, group):
     _run(pa, w)
 
 
+@pytest.mark.parametrize("block_size", [8, 16, 64])
+@pytest.mark.parametrize("group,head_dim", [(8, 128), (4, 256)])
+def test_fp8_block_sizes_matrix_scores(pa, group, head_dim, block_size):
+    # shapes whose scores run on the matrix cores when blocks hold >= 16 keys
+    # (16-key loads); smaller blocks take the per-lane lookup path
+    w = wl.custom_decode(450 + block_size + group, LENS,
+                         num_blocks=2048 // block_size + 64, block_size=block_size,
+                         num_q_heads=2 * group, num_kv_heads=2, head_dim=head_dim,
+                         dtype=wl.BF16, name=f"fp8_mqk_bs{block_size}_g{group}_d{head_dim}")
+    _run(pa, w)
+
+
 @pytest.mark.parametrize("block_size", [1, 4, 8, 32])
 def test_fp8_block_sizes(pa, block_size):
     # block sizes below the rows of one load instruction take the per-lane lookup path
