@@ -136,9 +136,6 @@ struct WaveCtx {
   static constexpr bool FP8 = sizeof(T) == 1;
   static constexpr uint32_t kChunkStride = LPR * 16;  // bytes between a lane's chunks
   static constexpr int QW = FP8 ? 2 : 1;  // 16-byte pieces of one chunk of the bf16 query
-  // fp8 with up to 4 heads per KV head and head_dim <= 128: the query in
-  // registers (see qf); otherwise in LDS like the other types (registers
-  // would not hold it)
   // fp8 scores on the matrix cores: S = Q K^T with v_mfma_f32_16x16x32_bf16
   // per group of 16 keys (query heads as the 16 rows, G of them real; keys
   // as the columns; 32 dims a step).  Lane l loads 16 codes of key l % 16 --
@@ -152,6 +149,9 @@ struct WaveCtx {
   static constexpr int KG = TT / 16;  // 16-key groups per tile
   static constexpr int LPK = D / 64;  // K loads per group (64 codes per 16 lanes)
   static constexpr int NU = D / 32;   // matrix steps per group
+  // fp8 scores on the vector units: the query in registers as bfloat16 pairs
+  // (qp) up to PA_FP8_QREG_MAX_G heads and PA_FP8_QREG_MAX_D dims, else in
+  // LDS like the other types
   static constexpr bool QREG = FP8 && !MQK && G <= PA_FP8_QREG_MAX_G && D <= PA_FP8_QREG_MAX_D;
 
   struct Tile {
@@ -163,7 +163,7 @@ struct WaveCtx {
   // The current query lives in LDS, not registers: [G][CPL][LPR] 16-byte
   // chunks per wave (fp32: pre-scaled), read back once per tile; the lanes
   // of one chunk column read the same address (broadcast).  (fp8: registers,
-  // see qf.)
+  // see qp and qa.)
   static constexpr int kQChunks = QREG ? 1 : G * CPL * LPR * QW;
 
   const DecodeArgs& a;
