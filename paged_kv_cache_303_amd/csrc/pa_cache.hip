@@ -132,17 +132,21 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ kp,
 
 // One wave per (query token, query head); kReduceWaves heads per workgroup.
 // Lane l owns dims [VEC l, VEC l + VEC) of the row (VEC = max(D / 64, 1)) and
-// the weight exp(lse_p - m) of partition p = l (per 64 partitions); the
-// partitions' rows are loaded 8 or 16 at a time, all in flight together
-// (the first batch already while the weights are computed), and summed in
-// partition order with the weights read from their lanes.
+// the weight exp(lse_p - m) of partition p = l (per 64 partitions).  The
+// row's first two partitions and its first 64 lse values are requested at
+// once, before the query's partition count is known (they lie inside the
+// row's slots whatever that count is, and are used only below it): a query
+// of a prefill chunk has at most two partitions, so it needs no other load.
+// Further partitions are loaded 8 or 16 rows at a time, all in flight
+// together, and summed in partition order with the weights read from their
+// lanes.
 constexpr int kReduceWaves = 4;
 
 template <int VEC>
-__device__ __forceinline__ void reduce_row(const ReduceArgs& a, int64_t row, int nparts,
-                                           int lane) {
+__device__ __forceinline__ void reduce_query(const ReduceArgs& a, int j, int h, int lane) {
   constexpr int kReduceBatch = VEC >= 4 ? 8 : 16;  // rows in flight per lane
   const int D = a.head_dim;
+  const int64_t row = (int64_t)j * a.num_q_heads + h;
   const float* lse = a.part_lse + row * a.max_partitions;
   const float* po = a.part_o + row * a.max_partitions * D;
   const int d0 = lane * VEC;
@@ -171,14 +175,65 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs& a, int64_t row, int
       }
     }
   };
-  // the first batch of rows is requested before the weights are known
-  float first[kReduceBatch][VEC];
-  load_batch(0, nparts, first);
-  float m = -INFINITY;
-  for (int p = lane; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
+  // ---- requested before the partition count: partitions 0 and 1, lse[lane]
+  float pre[2][VEC];
+  load(0, pre[0]);
+  if (a.max_partitions > 1) {
+    load(1, pre[1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) pre[1][e] = 0.f;
+  }
+  const float lse_lane = lane < a.max_partitions ? lse[lane] : -INFINITY;
+
+  // ---- the query's sequence and partition count ------------------------------
+  int q_first = j, q_len = 1, len = 0;
+  if (a.cu_q_lens != nullptr) {
+    // the last b with cu_q_lens[b] <= j: each round reads 64 entries at once
+    // (one per lane) and keeps the span between the last two that qualify;
+    // the last round (one entry per lane) also reads each candidate's next
+    // entry and length, so the sequence is known when the round ends
+    int lo = 0, n = a.num_seqs;  // b in [lo, lo + n)
+    for (;;) {
+      const int step = (n + kWave - 1) / kWave;
+      const int i = lo + lane * step;
+      const bool in = lane * step < n;
+      const int ci = in ? a.cu_q_lens[i] : 0;
+      int cn = 0, sl = 0;
+      if (step == 1 && in) {
+        cn = a.cu_q_lens[i + 1];
+        sl = a.seq_lens[i];
+      }
+      const int k = 63 - __builtin_clzll(__ballot(in && ci <= j) | 1ull);  // last that qualifies
+      if (step == 1) {
+        q_first = __builtin_amdgcn_readlane(ci, k);
+        q_len = __builtin_amdgcn_readlane(cn, k) - q_first;
+        len = max(__builtin_amdgcn_readlane(sl, k), 0);
+        break;
+      }
+      lo += k * step;
+      n = min(step, n - k * step);
+    }
+  } else {
+    len = max(a.seq_lens[j], 0);
+  }
+  const int key_end = len - q_len + (j - q_first) + 1;
+  // a decode query has ceil(key_end / P) partitions; each query of a prefill
+  // chunk (q_len > 1) has two split at half the cached context (in 32-key
+  // tiles), or one when that half is empty
+  int nparts = 0;
+  if (key_end > 0) {
+    if (q_len > 1) nparts = 32 * (((len - q_len + 31) / 32) / 2) > 0 ? 2 : 1;
+    else nparts = (key_end + a.partition_size - 1) / a.partition_size;
+  }
+  nparts = min(nparts, a.max_partitions);
+
+  // ---- weights exp(lse_p - m), their sum, the weighted rows ------------------
+  float m = lane < nparts ? lse_lane : -INFINITY;
+  for (int p = lane + kWave; p < nparts; p += kWave) m = fmaxf(m, lse[p]);
   m = reduce_levels<0, 6>(m, OpMax());
-  float wsum = 0.f;
-  for (int p = lane; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
+  float wsum = lane < nparts ? __expf(lse_lane - m) : 0.f;
+  for (int p = lane + kWave; p < nparts; p += kWave) wsum += __expf(lse[p] - m);
   wsum = reduce_levels<0, 6>(wsum, OpSum());
   const float inv = nparts > 0 ? 1.f / wsum : 0.f;
 
@@ -187,20 +242,25 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs& a, int64_t row, int
   for (int e = 0; e < VEC; ++e) o[e] = 0.f;
   for (int pc = 0; pc < nparts; pc += kWave) {
     const int n = min(kWave, nparts - pc);
-    const float wl = lane < n ? __expf(lse[pc + lane] - m) : 0.f;
+    const float wl = lane < n ? __expf((pc == 0 ? lse_lane : lse[pc + lane]) - m) : 0.f;
     auto weight = [&](int p) {  // p is wave-uniform
       return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), p));
     };
-    for (int p = 0; p < n; p += kReduceBatch) {
-      float v[kReduceBatch][VEC];
-      if (pc + p == 0) {
+    int p = 0;
+    if (pc == 0) {  // partitions 0 and 1: already loaded
 #pragma unroll
-        for (int i = 0; i < kReduceBatch; ++i)
+      for (int i = 0; i < 2; ++i) {
+        if (i < n) {
+          const float w = weight(i);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) v[i][e] = first[i][e];
-      } else {
-        load_batch(pc + p, pc + n, v);
+          for (int e = 0; e < VEC; ++e) o[e] = fmaf(w, pre[i][e], o[e]);
+        }
       }
+      p = 2;
+    }
+    for (; p < n; p += kReduceBatch) {
+      float v[kReduceBatch][VEC];
+      load_batch(pc + p, pc + n, v);
 #pragma unroll
       for (int i = 0; i < kReduceBatch; ++i) {
         if (p + i < n) {
@@ -230,41 +290,10 @@ __global__ __launch_bounds__(kReduceWaves * kWave) void reduce_kernel(ReduceArgs
   const int lane = threadIdx.x & (kWave - 1);
   const int h = blockIdx.y * kReduceWaves + threadIdx.x / kWave;
   if (h >= a.num_q_heads) return;
-
-  int b = j, q_first = j, q_len = 1;
-  if (a.cu_q_lens != nullptr) {
-    // the last b with cu_q_lens[b] <= j: each round reads 64 entries at once
-    // (one per lane) and keeps the span between the last two that qualify
-    int lo = 0, n = a.num_seqs;  // b in [lo, lo + n)
-    while (n > 1) {
-      const int step = (n + kWave - 1) / kWave;
-      const int i = lo + lane * step;
-      const bool le = lane * step < n && a.cu_q_lens[i] <= j;
-      const int k = 63 - __builtin_clzll(__ballot(le) | 1ull);  // last lane that qualifies
-      lo += k * step;
-      n = min(step, n - k * step);
-    }
-    b = lo;
-    q_first = a.cu_q_lens[b];
-    q_len = a.cu_q_lens[b + 1] - q_first;
-  }
-  const int len = max(a.seq_lens[b], 0);
-  const int key_end = len - q_len + (j - q_first) + 1;
-  // a decode query has ceil(key_end / P) partitions; each query of a prefill
-  // chunk (q_len > 1) has two split at half the cached context (in 32-key
-  // tiles), or one when that half is empty
-  int nparts = 0;
-  if (key_end > 0) {
-    if (q_len > 1) nparts = 32 * (((len - q_len + 31) / 32) / 2) > 0 ? 2 : 1;
-    else nparts = (key_end + a.partition_size - 1) / a.partition_size;
-  }
-  nparts = min(nparts, a.max_partitions);
-
-  const int64_t row = (int64_t)j * a.num_q_heads + h;
   switch (a.head_dim) {
-    case 256: reduce_row<4>(a, row, nparts, lane); break;
-    case 128: reduce_row<2>(a, row, nparts, lane); break;
-    default: reduce_row<1>(a, row, nparts, lane); break;  // 32, 64
+    case 256: reduce_query<4>(a, j, h, lane); break;
+    case 128: reduce_query<2>(a, j, h, lane); break;
+    default: reduce_query<1>(a, j, h, lane); break;  // 32, 64
   }
 }
 
