@@ -842,6 +842,22 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 1) void split_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int w = wave_id();
 
+  // ---- work queues ----------------------------------------------------------------
+  // ctrl[q]: claims made on queue q (item block index); ctrl[kQueues]: finished
+  // workgroups.  Thread 0 claims the next item of its current queue while the
+  // workgroup runs the current one (the first claim already here, in flight
+  // with the loads of the per-sequence work below).  When that queue is
+  // spent, wave 0 reads every counter at once (one lane per queue) and claims
+  // from the first queue after its own that still has blocks, until none has.
+  int* ctrl = a.queue;
+  const int home = blockIdx.x % kQueues;
+  auto claim = [&](int q) {
+    return __hip_atomic_fetch_add(&ctrl[q], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  int q_cur = home;
+  int next = -1;  // thread 0: the claim in flight on q_cur
+  if (threadIdx.x == 0) next = claim(q_cur);
+
   // ---- work per sequence ------------------------------------------------------------
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
     const int q_len = a.cu_q_lens ? a.cu_q_lens[b + 1] - a.cu_q_lens[b] : 1;
@@ -867,20 +883,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave, 1) void split_kernel(
   const int nbd = (nd + kQueues - 1) / kQueues, nbp = (np + kQueues - 1) / kQueues;
   const int nb = nbd + nbp;  // blocks of kQueues items; queue q holds position q of each
 
-  // ---- work queues ----------------------------------------------------------------
-  // ctrl[q]: claims made on queue q (item block index); ctrl[kQueues]: finished
-  // workgroups.  Thread 0 claims the next item of its current queue while the
-  // workgroup runs the current one.  When that queue is spent, wave 0 reads
-  // every counter at once (one lane per queue) and claims from the first queue
-  // after its own that still has blocks, until none has.
-  int* ctrl = a.queue;
-  const int home = blockIdx.x % kQueues;
-  auto claim = [&](int q) {
-    return __hip_atomic_fetch_add(&ctrl[q], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  int q_cur = home;
-  int next = -1;  // thread 0: the claim in flight on q_cur
-  if (threadIdx.x == 0) next = claim(q_cur);
+  // ---- work queues: claims as set up above ------------------------------------------
   for (;;) {
     if (w == 0) {
       int item = -1;
