@@ -243,6 +243,18 @@ def test_reduce_many_partitions(pa, dtype, head_dim):
     _check_all_paths(pa, w, st_p, st_o, partitions=(None,))
 
 
+@pytest.mark.parametrize("q_lens", [None, [1, 1, 40, 1]])
+def test_reduce_odd_head_count(pa, q_lens):
+    """An odd query-head count (the merge's workgroups cover four heads, the
+    last one partly): decode queries with many partitions and, with q_lens, a
+    prefill chunk's queries (two partitions each)."""
+    w = wl.custom_decode(33, [1100, 257, 600, 1], num_blocks=512, block_size=16,
+                         num_q_heads=3, num_kv_heads=3, head_dim=128, dtype=wl.BF16,
+                         q_lens=q_lens, partition_size=16, name="odd_heads")
+    st_p, st_o = _both(pa, w)
+    _check_all_paths(pa, w, st_p, st_o, partitions=(None,))
+
+
 @pytest.mark.parametrize("lens", [
     [3000, 1, 2],                      # one sequence spans many slices
     [1] * 300,                         # fewer tiles than slices
