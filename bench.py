@@ -267,8 +267,8 @@ def _fp8_decode(binding, runner, w, st, new_slots, q, bt_d, sl_d, args, dev):
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc = torch.empty(shape, dtype=torch.uint8, device=dev)
     vc = torch.empty(shape, dtype=torch.uint8, device=dev)
-    ks = torch.empty(shape[:3], dtype=torch.float32, device=dev)
-    vs = torch.empty(shape[:3], dtype=torch.float32, device=dev)
+    ks = torch.empty(binding.fp8_scale_shape(kc), dtype=torch.float32, device=dev)
+    vs = torch.empty(binding.fp8_scale_shape(kc), dtype=torch.float32, device=dev)
     ctx = np.concatenate([np.asarray(sl, np.int32) for _, sl, _ in st["log"]])
     all_slots = torch.from_numpy(np.concatenate([ctx, new_slots]).astype(np.int32)).to(dev)
     binding.kv_write_fp8(kc, vc, ks, vs, runner.to_device(w.k_tokens, w.dtype, dev),

@@ -61,7 +61,8 @@ typedef enum {
 /* Pool element types.  PA_FP8: e4m3 codes (1 byte: sign, 4 exponent bits of
  * bias 7, 3 mantissa bits; largest finite 448; 0x7F/0xFF are NaN) with one
  * float32 scale per (token, KV head) in separate scale pools
- * [num_blocks, block_size, num_kv_heads]; the stored value is code * scale.
+ * [num_blocks, num_kv_heads, block_size] (the rows of one head contiguous);
+ * the stored value is code * scale.
  * Queries and outputs of fp8 pools are bfloat16. */
 typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
@@ -161,8 +162,9 @@ pa_status pa_decode_workspace_size(const pa_kv_layout* layout, int32_t num_seqs,
  * dequantized by multiplying the scale back; the page's formula is lost, the
  * reading here is symmetric absmax).  layout->dtype must be PA_FP8; k_pool
  * and v_pool hold e4m3 codes [num_blocks, block_size, num_kv_heads,
- * head_dim], k_scale and v_scale float32 [num_blocks, block_size,
- * num_kv_heads], all caller-owned device memory.
+ * head_dim], k_scale and v_scale float32 [num_blocks, num_kv_heads,
+ * block_size] (the scale of row r of block b for head h at (b, h, r)), all
+ * caller-owned device memory.
  *
  * Quantizing cache write: for every token t with slot s = slot_mapping[t]
  * in [0, num_blocks*block_size) and every KV head, the row x (head_dim

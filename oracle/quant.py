@@ -97,12 +97,25 @@ def dequantize(codes, scales) -> np.ndarray:
     return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 
+def scale_pool_shape(num_blocks: int, block_size: int, num_kv_heads: int):
+    """Shape of a scale pool: one float32 per (block, KV head, row of the block),
+    the rows of one head contiguous (``[NB, Hkv, bs]``)."""
+    return (num_blocks, num_kv_heads, block_size)
+
+
+def dequantize_pool(codes, scales) -> np.ndarray:
+    """float64 values of a code pool ``[NB, bs, Hkv, D]`` with its scale pool
+    ``[NB, Hkv, bs]``: ``code * scale`` of the same (block, row, head)."""
+    return dequantize(codes, np.asarray(scales).transpose(0, 2, 1))
+
+
 def kv_write_fp8(k_codes, v_codes, k_scales, v_scales, k_new, v_new, slot_mapping,
                  block_size: int) -> None:
     """In place: quantize token t's K and V rows (per KV head) into slot s >= 0.
 
-    Pools: codes ``[NB, bs, Hkv, D]`` uint8, scales ``[NB, bs, Hkv]`` float32;
-    new tokens ``[T, Hkv, D]`` as float32 values (bf16 inputs widened).
+    Pools: codes ``[NB, bs, Hkv, D]`` uint8, scales ``[NB, Hkv, bs]`` float32
+    (``scale_pool_shape``); new tokens ``[T, Hkv, D]`` as float32 values
+    (bf16 inputs widened).
     """
     kc, ks = quantize_rows(k_new)
     vc, vs = quantize_rows(v_new)
@@ -112,5 +125,5 @@ def kv_write_fp8(k_codes, v_codes, k_scales, v_scales, k_new, v_new, slot_mappin
         block, off = divmod(s, block_size)
         k_codes[block, off] = kc[t]
         v_codes[block, off] = vc[t]
-        k_scales[block, off] = ks[t]
-        v_scales[block, off] = vs[t]
+        k_scales[block, :, off] = ks[t]
+        v_scales[block, :, off] = vs[t]

@@ -185,14 +185,22 @@ def copy_blocks(k_pool, v_pool, pairs) -> None:
                                 int(pairs.shape[0]), _stream()))
 
 
+def fp8_scale_shape(k_pool) -> tuple:
+    """Shape of the scale pools of an e4m3 code pool ``[NB, bs, Hkv, D]``:
+    ``[NB, Hkv, bs]`` (one float32 per block, KV head and row; a head's rows
+    contiguous)."""
+    nb, bs, hkv = (int(x) for x in k_pool.shape[:3])
+    return (nb, hkv, bs)
+
+
 def _fp8_pools(k_pool, v_pool, k_scale, v_scale):
     lay, kp, vp = _pools(k_pool, v_pool)
     if lay.dtype != PA_FP8:
         raise TypeError("fp8 pools are uint8 (e4m3 codes)")
-    shape = tuple(k_pool.shape[:3])
+    shape = fp8_scale_shape(k_pool)
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
         if tuple(t.shape) != shape:
-            raise ValueError(f"{name} must be [num_blocks, block_size, num_kv_heads]")
+            raise ValueError(f"{name} must be [num_blocks, num_kv_heads, block_size]")
     return lay, kp, vp, _dev(k_scale, "k_scale", torch.float32), \
         _dev(v_scale, "v_scale", torch.float32)
 

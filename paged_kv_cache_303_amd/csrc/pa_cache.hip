@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void kv_write_kernel(char* __restrict__ kp, ch
 __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
     uint8_t* __restrict__ kp, uint8_t* __restrict__ vp, float* __restrict__ ks,
     float* __restrict__ vs, const uint16_t* __restrict__ kn, const uint16_t* __restrict__ vn,
-    const int32_t* __restrict__ slots, int32_t num_kv_heads, int32_t head_dim, int64_t num_rows) {
+    const int32_t* __restrict__ slots, int32_t num_kv_heads, int32_t head_dim, int32_t log2_bs,
+    int64_t num_rows) {
   const int t = blockIdx.x;
   const int h = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
@@ -76,7 +77,9 @@ __global__ __launch_bounds__(64) void kv_write_fp8_kernel(
     }
     *(uint16_t*)(dst + d) = (uint16_t)codes;
   }
-  if (lane == 0) (is_v ? vs : ks)[s * num_kv_heads + h] = scale;
+  if (lane == 0)
+    (is_v ? vs : ks)[fp8_scale_index(s >> log2_bs, (int)(s & ((1 << log2_bs) - 1)), h,
+                                     num_kv_heads, log2_bs)] = scale;
 }
 
 constexpr int64_t kCopyChunk = 16384;  // bytes per workgroup
@@ -340,10 +343,12 @@ pa_status launch_kv_write_fp8(const pa_kv_layout& l, void* k_pool, void* v_pool,
                               const int32_t* slots, int32_t num_tokens, void* stream) {
   if (num_tokens == 0) return PA_OK;
   const int64_t num_rows = (int64_t)l.num_blocks * l.block_size;
+  int log2_bs = 0;  // block_size is a power of two (checked by the caller)
+  while ((1 << log2_bs) < l.block_size) ++log2_bs;
   hipLaunchKernelGGL(kv_write_fp8_kernel, dim3(num_tokens, l.num_kv_heads, 2), dim3(kWave), 0,
                      (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool, k_scale, v_scale,
                      (const uint16_t*)k_new, (const uint16_t*)v_new, slots, l.num_kv_heads,
-                     l.head_dim, num_rows);
+                     l.head_dim, log2_bs, num_rows);
   return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 

@@ -221,6 +221,15 @@ __device__ __forceinline__ void fp8x16_pairs_to_bf16x2(const uint4& wa, const ui
 }
 
 // Two floats to two e4m3 codes (low byte = a), nearest even.
+// Index of the scale of (physical block, row of the block, KV head) in an fp8
+// scale pool laid out [num_blocks][num_kv_heads][block_size]: the rows of one
+// head are contiguous, so the rows of one load instruction share one short
+// run of scales.
+__device__ __forceinline__ int64_t fp8_scale_index(int64_t phys, int row, int kvh,
+                                                   int num_kv_heads, int log2_bs) {
+  return ((phys * num_kv_heads + kvh) << log2_bs) + row;
+}
+
 __device__ __forceinline__ uint32_t f32x2_to_fp8(float a, float b) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }

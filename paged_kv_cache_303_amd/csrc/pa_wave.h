@@ -325,8 +325,8 @@ struct WaveCtx {
 #pragma unroll
           for (int ii = 0; ii < LPK; ++ii)
             tl.k[kg * LPK + ii][0] = buffer_load16_nt(kr, k_off + 64 * ii, (uint32_t)r0 * row_bytes);
-          tl.ks[kg] = a.k_scale[(((int64_t)phys << a.log2_bs) + r0 + (lane & 15)) *
-                                    a.num_kv_heads + kvh];
+          tl.ks[kg] = a.k_scale[fp8_scale_index(phys, r0 + (lane & 15), kvh, a.num_kv_heads,
+                                                a.log2_bs)];
         }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -335,8 +335,8 @@ struct WaveCtx {
           const __amdgpu_buffer_rsrc_t vr =
               buffer_rsrc(vp + phys * block_bytes, (uint32_t)block_bytes);
           tl.v[i][0] = buffer_load16_nt(vr, lane_off, row);
-          tl.vs[i] = a.v_scale[(((int64_t)phys << a.log2_bs) + ((t0 + i * TPI) & bs_mask) + tg) *
-                                   a.num_kv_heads + kvh];
+          tl.vs[i] = a.v_scale[fp8_scale_index(phys, ((t0 + i * TPI) & bs_mask) + tg, kvh,
+                                               a.num_kv_heads, a.log2_bs)];
         }
         return;
       }
@@ -352,10 +352,10 @@ struct WaveCtx {
 #pragma unroll
         for (int k = 0; k < CPL; ++k) tl.v[i][k] = buffer_load16_nt(vr, lane_off + k * kChunkStride, row);
         if constexpr (FP8) {  // this lane's row: tg rows into the instruction's rows
-          const int64_t srow =
-              ((int64_t)phys << a.log2_bs) + ((t0 + i * TPI) & bs_mask) + tg;
-          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
-          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
+          const int64_t si = fp8_scale_index(phys, ((t0 + i * TPI) & bs_mask) + tg, kvh,
+                                             a.num_kv_heads, a.log2_bs);
+          tl.ks[i] = a.k_scale[si];
+          tl.vs[i] = a.v_scale[si];
         }
       }
     } else {
@@ -371,9 +371,10 @@ struct WaveCtx {
 #pragma unroll
         for (int k = 0; k < CPL; ++k) tl.v[i][k] = load16_nt(vb + k * kChunkStride);
         if constexpr (FP8) {
-          const int64_t srow = ((int64_t)phys << a.log2_bs) + (tok & bs_mask);
-          tl.ks[i] = a.k_scale[srow * a.num_kv_heads + kvh];
-          tl.vs[i] = a.v_scale[srow * a.num_kv_heads + kvh];
+          const int64_t si =
+              fp8_scale_index(phys, tok & bs_mask, kvh, a.num_kv_heads, a.log2_bs);
+          tl.ks[i] = a.k_scale[si];
+          tl.vs[i] = a.v_scale[si];
         }
       }
     }

@@ -40,8 +40,8 @@ def _gpu_fp8(pa, w, st):
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc = torch.full(shape, NAN_CODE, dtype=torch.uint8, device=dev)
     vc = torch.full(shape, NAN_CODE, dtype=torch.uint8, device=dev)
-    ks = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev)
-    vs = torch.full(shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    ks = torch.full(binding.fp8_scale_shape(kc), float("nan"), dtype=torch.float32, device=dev)
+    vs = torch.full(binding.fp8_scale_shape(kc), float("nan"), dtype=torch.float32, device=dev)
     slots = torch.from_numpy(_slots(st["log"])).to(dev)
     binding.kv_write_fp8(kc, vc, ks, vs, runner.to_device(w.k_tokens, "bf16", dev),
                          runner.to_device(w.v_tokens, "bf16", dev), slots)
@@ -52,8 +52,8 @@ def _oracle_fp8(w, st_o):
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc = np.full(shape, NAN_CODE, np.uint8)
     vc = np.full(shape, NAN_CODE, np.uint8)
-    ks = np.full(shape[:3], np.nan, np.float32)
-    vs = np.full(shape[:3], np.nan, np.float32)
+    ks = np.full(oq.scale_pool_shape(*shape[:3]), np.nan, np.float32)
+    vs = np.full(oq.scale_pool_shape(*shape[:3]), np.nan, np.float32)
     k_new = bf16_bits_to_f64(w.k_tokens).astype(np.float32)  # exact widening
     v_new = bf16_bits_to_f64(w.v_tokens).astype(np.float32)
     oq.kv_write_fp8(kc, vc, ks, vs, k_new, v_new, _slots(st_o["log"]), w.block_size)
@@ -83,8 +83,8 @@ def _run(pa, w, tokens=None):
     renum = np.full(w.num_blocks, -1, np.int32)
     renum[used] = np.arange(len(used), dtype=np.int32)
     ctab = np.where(tables >= 0, renum[np.maximum(tables, 0)], -1)
-    ref = paged_attention(w.q, oq.dequantize(o[0][used], o[2][used]),
-                          oq.dequantize(o[1][used], o[3][used]), ctab, st_o["seq_lens"],
+    ref = paged_attention(w.q, oq.dequantize_pool(o[0][used], o[2][used]),
+                          oq.dequantize_pool(o[1][used], o[3][used]), ctab, st_o["seq_lens"],
                           w.scale, w.block_size, cu_q_lens=w.cu_q_lens, tokens=tokens)
     args = (st["q"], g[0], g[1], g[2], g[3], st["block_tables"], st["seq_lens"], w.scale)
     stats = {}
@@ -197,8 +197,8 @@ def test_fp8_copy_blocks(pa, shape):
     gen = torch.Generator().manual_seed(0)
     kc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)
     vc = torch.randint(0, 126, shape, generator=gen, dtype=torch.uint8).to(dev)
-    ks = torch.rand(shape[:3], generator=gen).to(dev)
-    vs = torch.rand(shape[:3], generator=gen).to(dev)
+    ks = torch.rand(binding.fp8_scale_shape(kc), generator=gen).to(dev)
+    vs = torch.rand(binding.fp8_scale_shape(kc), generator=gen).to(dev)
     k0, v0, ks0, vs0 = kc.clone(), vc.clone(), ks.clone(), vs.clone()
     pairs = torch.tensor([[1, 5], [2, 6]], dtype=torch.int32, device=dev)
     binding.copy_blocks_fp8(kc, vc, ks, vs, pairs)
@@ -213,7 +213,7 @@ def test_fp8_copy_blocks(pa, shape):
 def test_fp8_rejections(pa):
     binding, runner, dev = pa
     k = torch.zeros((4, 16, 2, 32), dtype=torch.uint8, device=dev)
-    s = torch.zeros((4, 16, 2), dtype=torch.float32, device=dev)
+    s = torch.zeros(binding.fp8_scale_shape(k), dtype=torch.float32, device=dev)
     q = torch.zeros((1, 4, 32), dtype=torch.bfloat16, device=dev)
     bt = torch.zeros((1, 1), dtype=torch.int32, device=dev)
     sl = torch.ones((1,), dtype=torch.int32, device=dev)

@@ -88,8 +88,8 @@ def test_swap_round_trip_fp8_codes_and_scales(pa):
     shape = tuple(st["k_pool"].shape)
     kc = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
     vc = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
-    ks = torch.full(shape[:3], float("nan"), device=dev)
-    vs = torch.full(shape[:3], float("nan"), device=dev)
+    ks = torch.full(binding.fp8_scale_shape(kc), float("nan"), device=dev)
+    vs = torch.full(binding.fp8_scale_shape(kc), float("nan"), device=dev)
     slots = np.concatenate([np.asarray(s, np.int32) for _, s, _ in st["log"]])
     binding.kv_write_fp8(kc, vc, ks, vs, runner.to_device(w.k_tokens, "bf16", dev),
                          runner.to_device(w.v_tokens, "bf16", dev),
@@ -102,7 +102,8 @@ def test_swap_round_trip_fp8_codes_and_scales(pa):
     dev_ids = tables[b, :nblk].tolist()
     hk = torch.zeros((nblk,) + shape[1:], dtype=torch.uint8, pin_memory=True)
     hv = torch.zeros_like(hk).pin_memory()
-    hks = torch.zeros((nblk,) + shape[1:3], dtype=torch.float32, pin_memory=True)
+    hks = torch.zeros((nblk,) + binding.fp8_scale_shape(kc)[1:], dtype=torch.float32,
+                      pin_memory=True)
     hvs = torch.zeros_like(hks).pin_memory()
     out_pairs = torch.tensor([[d, i] for i, d in enumerate(dev_ids)], dtype=torch.int32).to(dev)
     binding.swap_blocks(hk, hv, kc, vc, out_pairs)

@@ -112,13 +112,16 @@ def test_kv_write_fp8_places_rows():
     nb, bs, hkv, d = 4, 4, 2, 16
     kc = np.zeros((nb, bs, hkv, d), np.uint8)
     vc = np.zeros_like(kc)
-    ks = np.full((nb, bs, hkv), np.nan, np.float32)
+    ks = np.full(qn.scale_pool_shape(nb, bs, hkv), np.nan, np.float32)  # [NB, Hkv, bs]
     vs = ks.copy()
     k_new = rng.standard_normal((3, hkv, d)).astype(np.float32)
     v_new = rng.standard_normal((3, hkv, d)).astype(np.float32)
     qn.kv_write_fp8(kc, vc, ks, vs, k_new, v_new, [5, -1, 14], bs)
     c0, s0 = qn.quantize_rows(k_new[0])
-    assert np.array_equal(kc[1, 1], c0) and np.array_equal(ks[1, 1], s0)
+    assert np.array_equal(kc[1, 1], c0) and np.array_equal(ks[1, :, 1], s0)
     c2, s2 = qn.quantize_rows(v_new[2])
-    assert np.array_equal(vc[3, 2], c2) and np.array_equal(vs[3, 2], s2)
+    assert np.array_equal(vc[3, 2], c2) and np.array_equal(vs[3, :, 2], s2)
     assert np.isnan(ks).sum() == (nb * bs - 2) * hkv  # only the two slots written
+    # the pool dequantizes row by row: slot 5's K values are its codes times its scales
+    deq = qn.dequantize_pool(kc, ks)
+    assert np.array_equal(deq[1, 1], qn.dequantize(c0, s0))
