@@ -94,23 +94,33 @@ __device__ __forceinline__ int uniform_lds(const int* p) { return __builtin_amdg
 // Work units of a sequence in the balanced decode's static slicing: its tiles
 // plus the cost of the pipeline restart at every sequence a slice holds
 // (query load, first block-table lookups and gathers, and the final
-// cross-lane combine and store), PA_SEQ_COST_TOKENS tokens' worth of tiles.
-// Per-wave timestamps on MI355X put one restart at 5-7 us; a sweep over 0..6
-// tiles of 16 tokens on the batch-256 GQA decode is fastest at 4 (2% below
-// 0).  The extra units come first: sequence b occupies units
+// cross-lane combine and store), a fixed number of tokens' worth of tiles:
+// PA_SEQ_COST_TOKENS for bf16 and fp32 pools, PA_FP8_SEQ_COST_TOKENS for fp8.
+// Per-wave timestamps on MI355X put one restart at 5-7 us.  On the batch-256
+// GQA decode with 32-token tiles, 96 tokens beats 64 for bf16 (the kv_write +
+// decode step 0.2845 -> 0.2825 ms, median of three pairs) while fp8 is
+// fastest at 64 (0.1708 against 0.1720 ms at 96); 32 and 128 are slower for
+// both.  The extra units come first: sequence b occupies units
 // [cum[b], cum[b+1]), its tiles are the last tiles(b) of them, and an empty
 // sequence has none.
 #ifndef PA_SEQ_COST_TOKENS
-#define PA_SEQ_COST_TOKENS 64
+#define PA_SEQ_COST_TOKENS 96
 #endif
+#ifndef PA_FP8_SEQ_COST_TOKENS
+#define PA_FP8_SEQ_COST_TOKENS 64
+#endif
+// Restart cost in units of TT-token tiles.
+template <typename T, int TT>
+constexpr int seq_cost_tiles() {
+  return ((sizeof(T) == 1 ? PA_FP8_SEQ_COST_TOKENS : PA_SEQ_COST_TOKENS) + TT - 1) / TT;
+}
 
 // Prefix sums of work units per sequence into LDS: ends[b] = len_b (clamped
 // to the table's capacity), cum[b] = units of sequences 0..b-1 (TT tokens a
 // tile).  Every thread loads lengths (one memory round trip), wave 0 scans.
 // Ends with a workgroup barrier.
-template <int TT>
+template <int TT, int kSeqCost>
 __device__ void tile_prefix(const DecodeArgs& a, int* cum, int* ends) {
-  constexpr int kSeqCost = (PA_SEQ_COST_TOKENS + TT - 1) / TT;
   const int B = a.num_seqs;
   const int cap = a.max_blocks << a.log2_bs;
   for (int i = threadIdx.x; i < B; i += blockDim.x) {
@@ -180,8 +190,8 @@ __global__ __launch_bounds__(kStreamWaves * kWave, 1) void decode_stream_kernel(
   const int r = blockIdx.x / groups;
   const int kvh = (blockIdx.x % groups) * a.waves_per_group + wave_id();
 
-  tile_prefix<TT>(a, cum, ends);
-  constexpr int kSeqCost = (PA_SEQ_COST_TOKENS + TT - 1) / TT;
+  constexpr int kSeqCost = seq_cost_tiles<T, TT>();
+  tile_prefix<TT, kSeqCost>(a, cum, ends);
   const int64_t total = uniform_lds(&cum[B]);
   // slices actually used: at most one per tile, so none is empty
   const int64_t R = min((int64_t)s.num_slices, total);
