@@ -93,10 +93,12 @@ constexpr size_t kScratchBytes = (size_t)8 << 20;
 pa_status scratch_buffer(void** ptr);
 // Split first pass: one persistent launch over a work list of decode
 // partitions and (bf16, head_dim <= 128) matrix-core prefill row tiles;
-// writes partition p of every single-query sequence's query and partition 0
-// (all keys) of every query of a multi-query sequence.
+// writes partition p of every single-query sequence's query, and for every
+// query of a multi-query sequence its two partitions (keys before and from
+// the split point of half the cached context), or partition 0 with all its
+// keys when that split point is 0.
 constexpr int32_t kSplitMaxSeqs = 8192;  // sequences per launch (LDS prefix sums)
-constexpr int32_t kSplitQueueInts = 16;  // work-queue counters in the workspace
+constexpr int32_t kSplitQueueInts = 16;  // work-queue counters the control block reserves
 pa_status launch_split(const DecodeArgs& a, void* stream);
 pa_status launch_reduce(const ReduceArgs& a, void* stream);
 pa_status launch_kv_write(const pa_kv_layout& l, void* k_pool, void* v_pool, const void* k_new,

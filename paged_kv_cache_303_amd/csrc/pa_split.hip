@@ -59,6 +59,7 @@ using namespace wave;
 
 constexpr int kSplitWaves = 8;     // waves per workgroup
 constexpr int kQueues = 8;         // work queues (one per XCD)
+static_assert(kQueues + 1 <= kSplitQueueInts, "queue and finish counters fit the control block");
 constexpr int kPfRowBlocks = 4;    // 32-row blocks per prefill item
 constexpr int kPfKeySplit = 2;     // key halves per prefill item
 constexpr int kPfRows = 32 * kPfRowBlocks;
