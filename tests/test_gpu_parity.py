@@ -232,6 +232,39 @@ def test_split_partials_match_oracle(pa, dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_split_many_rounds(pa, dtype):
+    """A split launch of decode steps only with more than two partitions per
+    wave of the grid (about 6,000 (partition, KV head) units against 2,048
+    resident waves on 256 compute units), so that every workgroup takes
+    several rounds of decode items from the work queues.  Every partial is
+    compared with the oracle's, with odd and even partition counts and
+    lengths off the partition grid among them, and then the merged output of
+    every path."""
+    binding, runner, _ = pa
+    lens = [int(x) for x in np.random.default_rng(71).integers(600, 2000, size=20)]
+    lens += [31, 32, 33, 64, 65, 96]
+    w = wl.custom_decode(71, lens, num_blocks=2560, block_size=16, num_q_heads=32,
+                         num_kv_heads=8, head_dim=128, dtype=dtype, partition_size=32,
+                         name="many_rounds")
+    st_p, st_o = _both(pa, w)
+    o_ref, lse_ref, nparts = orun.partials(w, st_o)
+    assert sum(nparts) * w.num_kv_heads >= 2 * 2048
+    ws = binding.decode_split(st_p["q"], st_p["k_pool"], st_p["v_pool"],
+                              st_p["block_tables"], st_p["seq_lens"], w.scale,
+                              partition_size=w.partition_size)
+    po, pl = to_f64(ws.part_o), to_f64(ws.part_lse)
+    tol = 1e-5 if dtype == wl.F32 else 1e-4
+    for j, n in enumerate(nparts):
+        np.testing.assert_allclose(pl[j, :, :n], lse_ref[j, :, :n], rtol=0, atol=tol)
+        if dtype == wl.F32:
+            np.testing.assert_allclose(po[j, :, :n], o_ref[j, :, :n], rtol=0, atol=tol)
+        else:  # bf16 probabilities in the P V products (fp32 accumulation)
+            d = np.abs(po[j, :, :n] - o_ref[j, :, :n])
+            assert (d <= 1e-2 + 2e-2 * np.abs(o_ref[j, :, :n])).all(), (j, d.max())
+    _check_all_paths(pa, w, st_p, st_o, partitions=(None,))
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
 @pytest.mark.parametrize("head_dim", [32, 128, 256])
 def test_reduce_many_partitions(pa, dtype, head_dim):
     """More partitions than a wave has lanes (the merge takes them 64 at a time),
